@@ -1,0 +1,275 @@
+/*
+ * h3_oracle.c -- plain fp64 CPU reference for the arithmetic steps of the
+ * Ulysses H3 hot path.  TEST INFRASTRUCTURE ONLY: it is loaded by tests/,
+ * by the smoke check and by the CPU-baseline leg of bench.py, never by the
+ * product library.  It shares no code, header or constant with the HIP path.
+ *
+ * Everything is written for clarity, not speed: no blocking, no fusion, no
+ * reordering beyond the definitions below.  The only concession to size is
+ * that callers pick which rows to evaluate, so a huge problem can be checked
+ * on a sample of rows, and that independent rows run on several threads.
+ *
+ * Inputs are raw bfloat16 bit patterns (uint16_t); each is widened exactly
+ * to double (bits << 16 is the IEEE float with the same value).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_bits_to_double(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Segment-masked attention over a packed multi-segment sequence.           */
+/*                                                                          */
+/* Source: "Distributed H3 Execution", introduction -- attention runs on    */
+/* the head side over the whole native packed sequence, with no semantic    */
+/* padding.  The pages do not write the score function out; the reading    */
+/* taken is plain softmax attention restricted to the query's own segment   */
+/* (block-diagonal, non-causal), logits scaled by 1/sqrt(head_dim) given    */
+/* by the caller.  For the gated QKVG form ("[perf] Harden Ulysses          */
+/* agreement ...", Problem and behavior: packed QKVG operands) the fourth   */
+/* plane G gates the output elementwise: o <- o * 1/(1+exp(-g)).            */
+/*                                                                          */
+/* Layout of q, k, v, g: [n_tokens][n_heads][head_dim], token-major.        */
+/* out: [n_rows][n_heads][head_dim] doubles, row r is token rows[r].        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *q, *k, *v, *g;
+    int64_t n_tokens;
+    int32_t n_heads, head_dim;
+    const int64_t *cu;
+    int32_t n_seg;
+    double scale;
+    const int64_t *rows;
+    int64_t n_rows;
+    double *out;
+    int64_t next_task;      /* shared work counter, guarded by lock */
+    pthread_mutex_t lock;
+    int status;
+} attn_job;
+
+/* Which segment holds token t: the s with cu[s] <= t < cu[s+1]. */
+static int32_t segment_of(const int64_t *cu, int32_t n_seg, int64_t t) {
+    for (int32_t s = 0; s < n_seg; ++s)
+        if (cu[s] <= t && t < cu[s + 1]) return s;
+    return -1;
+}
+
+static void attn_one(const attn_job *J, int64_t r, int32_t h, double *z, double *qrow, double *acc) {
+    const int32_t D = J->head_dim, H = J->n_heads;
+    const int64_t t = J->rows[r];
+    const int32_t s = segment_of(J->cu, J->n_seg, t);
+    const int64_t lo = J->cu[s], hi = J->cu[s + 1];
+    for (int32_t d = 0; d < D; ++d) qrow[d] = bf16_bits_to_double(J->q[(t * H + h) * D + d]);
+    /* logits z_u = scale * <q_t, k_u> for every key u of the same segment */
+    double zmax = -INFINITY;
+    for (int64_t u = lo; u < hi; ++u) {
+        double dot = 0.0;
+        const uint16_t *krow = J->k + (u * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) dot += qrow[d] * bf16_bits_to_double(krow[d]);
+        z[u - lo] = J->scale * dot;
+        if (z[u - lo] > zmax) zmax = z[u - lo];
+    }
+    /* softmax weights and the weighted sum of value rows */
+    double denom = 0.0;
+    for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int64_t u = lo; u < hi; ++u) {
+        double p = exp(z[u - lo] - zmax);
+        denom += p;
+        const uint16_t *vrow = J->v + (u * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) acc[d] += p * bf16_bits_to_double(vrow[d]);
+    }
+    double *o = J->out + (r * H + h) * D;
+    for (int32_t d = 0; d < D; ++d) {
+        double val = acc[d] / denom;
+        if (J->g) {
+            double gv = bf16_bits_to_double(J->g[(t * H + h) * D + d]);
+            val *= 1.0 / (1.0 + exp(-gv));
+        }
+        o[d] = val;
+    }
+}
+
+static void *attn_worker(void *arg) {
+    attn_job *J = (attn_job *)arg;
+    int64_t longest = 0;
+    for (int32_t s = 0; s < J->n_seg; ++s)
+        if (J->cu[s + 1] - J->cu[s] > longest) longest = J->cu[s + 1] - J->cu[s];
+    double *z = (double *)malloc(sizeof(double) * (size_t)(longest > 0 ? longest : 1));
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)J->head_dim);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->head_dim);
+    if (!z || !qrow || !acc) {
+        pthread_mutex_lock(&J->lock);
+        J->status = -2;
+        pthread_mutex_unlock(&J->lock);
+        free(z); free(qrow); free(acc);
+        return NULL;
+    }
+    const int64_t total = J->n_rows * J->n_heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t task = J->next_task++;
+        pthread_mutex_unlock(&J->lock);
+        if (task >= total) break;
+        attn_one(J, task / J->n_heads, (int32_t)(task % J->n_heads), z, qrow, acc);
+    }
+    free(z); free(qrow); free(acc);
+    return NULL;
+}
+
+static int run_threads(void *(*fn)(void *), void *job, int32_t n_threads) {
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 256) n_threads = 256;
+    pthread_t tid[256];
+    int started = 0;
+    for (int32_t i = 0; i < n_threads; ++i) {
+        if (pthread_create(&tid[i], NULL, fn, job) != 0) break;
+        ++started;
+    }
+    if (started == 0) fn(job);
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    return 0;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
+int h3o_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                  int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                  const int64_t *cu, int32_t n_seg, double scale,
+                  const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads) {
+    if (!q || !k || !v || !cu || !out || (n_rows > 0 && !rows)) return -1;
+    if (n_seg < 1 || n_heads < 1 || head_dim < 1 || cu[0] != 0 || cu[n_seg] != n_tokens) return -1;
+    for (int32_t s = 0; s < n_seg; ++s)
+        if (cu[s + 1] <= cu[s]) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= n_tokens) return -1;
+    attn_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.g = g;
+    J.n_tokens = n_tokens; J.n_heads = n_heads; J.head_dim = head_dim;
+    J.cu = cu; J.n_seg = n_seg; J.scale = scale;
+    J.rows = rows; J.n_rows = n_rows; J.out = out;
+    pthread_mutex_init(&J.lock, NULL);
+    run_threads(attn_worker, &J, n_threads);
+    pthread_mutex_destroy(&J.lock);
+    return J.status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-segment AdaLN modulation and residual gating on one token interval.  */
+/*                                                                          */
+/* Source: "Distributed H3 Execution", Partition Contract -- segment        */
+/* boundaries are clipped to the rank's token interval and rebased before   */
+/* AdaLN modulation and residual gating.  The clipped, rebased table is     */
+/* computed by the caller (oracle.clip_segments) and passed in as           */
+/* (seg_id[e], local_begin[e], local_end[e]).  The pages name the two ops   */
+/* but do not write them out; the reading taken is the usual DiT form:      */
+/*   MODULATE (mode 0): y = (x - mean) / sqrt(var + eps) * (1 + scale_s)    */
+/*                      + shift_s, mean and biased var over the channels;   */
+/*   GATE     (mode 1): y = x + gate_s * b.                                 */
+/* Parameters are rows of [n_segments][channels], picked by GLOBAL id s.    */
+/*                                                                          */
+/* x, b: [n_local][channels].  rows: local row indices to evaluate.         */
+/* out: [n_rows][channels] doubles.                                         */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t mode;
+    const uint16_t *x, *b, *shift, *scale, *gate;
+    int64_t n_local;
+    int32_t channels;
+    const int32_t *seg_id;
+    const int64_t *local_begin, *local_end;
+    int32_t n_entries;
+    double eps;
+    const int64_t *rows;
+    int64_t n_rows;
+    double *out;
+    int64_t next_task;
+    pthread_mutex_t lock;
+    int status;
+} adaln_job;
+
+static void adaln_one(const adaln_job *J, int64_t r) {
+    const int64_t i = J->rows[r];
+    const int32_t C = J->channels;
+    int32_t s = -1;
+    for (int32_t e = 0; e < J->n_entries; ++e)
+        if (J->local_begin[e] <= i && i < J->local_end[e]) { s = J->seg_id[e]; break; }
+    double *y = J->out + r * C;
+    if (s < 0) {                     /* row not covered by any segment: caller error */
+        for (int32_t c = 0; c < C; ++c) y[c] = NAN;
+        return;
+    }
+    const uint16_t *xr = J->x + i * C;
+    if (J->mode == 0) {
+        double mean = 0.0;
+        for (int32_t c = 0; c < C; ++c) mean += bf16_bits_to_double(xr[c]);
+        mean /= C;
+        double var = 0.0;
+        for (int32_t c = 0; c < C; ++c) {
+            double dev = bf16_bits_to_double(xr[c]) - mean;
+            var += dev * dev;
+        }
+        var /= C;
+        double inv = 1.0 / sqrt(var + J->eps);
+        for (int32_t c = 0; c < C; ++c) {
+            double xhat = (bf16_bits_to_double(xr[c]) - mean) * inv;
+            double sc = bf16_bits_to_double(J->scale[(int64_t)s * C + c]);
+            double sh = bf16_bits_to_double(J->shift[(int64_t)s * C + c]);
+            y[c] = xhat * (1.0 + sc) + sh;
+        }
+    } else {
+        const uint16_t *br = J->b + i * C;
+        for (int32_t c = 0; c < C; ++c) {
+            double gt = bf16_bits_to_double(J->gate[(int64_t)s * C + c]);
+            y[c] = bf16_bits_to_double(xr[c]) + gt * bf16_bits_to_double(br[c]);
+        }
+    }
+}
+
+static void *adaln_worker(void *arg) {
+    adaln_job *J = (adaln_job *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t task = J->next_task;
+        J->next_task += 64;
+        pthread_mutex_unlock(&J->lock);
+        if (task >= J->n_rows) break;
+        int64_t end = task + 64 < J->n_rows ? task + 64 : J->n_rows;
+        for (int64_t r = task; r < end; ++r) adaln_one(J, r);
+    }
+    return NULL;
+}
+
+int h3o_adaln_rows(int32_t mode, const uint16_t *x, const uint16_t *b,
+                   const uint16_t *shift, const uint16_t *scale, const uint16_t *gate,
+                   int64_t n_local, int32_t channels,
+                   const int32_t *seg_id, const int64_t *local_begin, const int64_t *local_end,
+                   int32_t n_entries, double eps,
+                   const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads) {
+    if (!x || !out || channels < 1 || n_entries < 0 || (n_rows > 0 && !rows)) return -1;
+    if (mode == 0 && (!shift || !scale)) return -1;
+    if (mode == 1 && (!b || !gate)) return -1;
+    if (mode != 0 && mode != 1) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= n_local) return -1;
+    adaln_job J;
+    memset(&J, 0, sizeof J);
+    J.mode = mode; J.x = x; J.b = b; J.shift = shift; J.scale = scale; J.gate = gate;
+    J.n_local = n_local; J.channels = channels;
+    J.seg_id = seg_id; J.local_begin = local_begin; J.local_end = local_end;
+    J.n_entries = n_entries; J.eps = eps;
+    J.rows = rows; J.n_rows = n_rows; J.out = out;
+    pthread_mutex_init(&J.lock, NULL);
+    run_threads(adaln_worker, &J, n_threads);
+    pthread_mutex_destroy(&J.lock);
+    return J.status;
+}

@@ -1,0 +1,383 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test ties one oracle function to something fixed from outside: the tables
+the pages print (tests/golden/), closed forms, invariants the pages name, and
+library routines that the method reduces to in special cases (torch's
+scaled-dot-product attention and layer norm in float64 on the CPU).  They are
+chosen so that a dropped term, a wrong sign or index, or a swapped operand in
+the oracle fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS
+from synth.inputs import normal_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# partition
+# ---------------------------------------------------------------------------
+
+def test_head_partition_matches_printed_table():
+    rows = _read_golden("head_partition.txt")
+    assert len(rows) == 4
+    for ranks, heads in rows:
+        expected = [int(h) for h in heads.split(",")]
+        got = oracle.partition(56, int(ranks))
+        assert [c for _, c in got] == expected
+        # ranks own consecutive head ranges starting at 0
+        assert [b for b, _ in got] == list(np.cumsum([0] + expected[:-1]))
+
+
+def test_token_window_identity():
+    """One bf16 plane of one rank's token shard at 250k / four ranks is the printed window."""
+    g = dict(_read_golden("transfer_window.txt"))
+    tokens, ranks = int(g["tokens"]), int(g["ranks"])
+    shard = oracle.partition(tokens, ranks)
+    assert all(c == 62500 for _, c in shard)
+    window = shard[0][1] * int(g["heads"]) * int(g["head_dim"]) * int(g["bytes_per_element"])
+    assert window == int(g["window_bytes"])
+    assert window < int(g["cap_bytes"])
+
+
+@pytest.mark.parametrize("total,parts", [(0, 1), (5, 6), (56, 57), (56, 0), (56, -1)])
+def test_partition_rejects_empty_parts(total, parts):
+    with pytest.raises(oracle.EmptyPartition):
+        oracle.partition(total, parts)
+
+
+def test_partition_properties_brute_force():
+    for total in range(1, 70):
+        for parts in range(1, total + 1):
+            got = oracle.partition(total, parts)
+            counts = [c for _, c in got]
+            assert sum(counts) == total
+            assert max(counts) - min(counts) <= 1
+            assert counts == sorted(counts, reverse=True)      # larger parts first
+            ends = [b + c for b, c in got]
+            assert [b for b, _ in got] == [0] + ends[:-1]       # contiguous, in rank order
+
+
+def test_token_split_of_8k_over_six():
+    got = oracle.partition(8192, 6)
+    assert [c for _, c in got] == [1366, 1366, 1365, 1365, 1365, 1365]
+    assert [b for b, _ in got] == [0, 1366, 2732, 4097, 5462, 6827]
+
+
+# ---------------------------------------------------------------------------
+# clip and rebase
+# ---------------------------------------------------------------------------
+
+def test_clip_worked_examples():
+    cu = [0, 96, 256, 512]
+    assert oracle.clip_segments(cu, 0, 256) == [(0, 0, 96), (1, 96, 256)]
+    assert oracle.clip_segments(cu, 256, 512) == [(2, 0, 256)]
+    assert oracle.clip_segments(cu, 50, 300) == [(0, 0, 46), (1, 46, 206), (2, 206, 250)]
+    # a segment boundary that equals a rank start gives no empty entry
+    cu4 = [0, 98304, 131072]
+    assert oracle.clip_segments(cu4, 98304, 131072) == [(1, 0, 32768)]
+    assert oracle.clip_segments(cu4, 65536, 98304) == [(0, 0, 32768)]
+
+
+def test_clip_brute_force_per_token():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        n = int(rng.integers(2, 60))
+        s = int(rng.integers(1, n + 1))
+        cuts = sorted(rng.choice(np.arange(1, n), size=s - 1, replace=False)) if s > 1 else []
+        cu = [0] + [int(c) for c in cuts] + [n]
+        a = int(rng.integers(0, n))
+        b = int(rng.integers(a + 1, n + 1))
+        table = oracle.clip_segments(cu, a, b)
+        for t in range(a, b):
+            global_seg = max(i for i in range(len(cu) - 1) if cu[i] <= t)
+            hits = [sid for sid, lo, hi in table if lo <= t - a < hi]
+            assert hits == [global_seg]
+        # pieces are disjoint, ordered and tile [0, b - a)
+        assert table[0][1] == 0 and table[-1][2] == b - a
+        for e0, e1 in zip(table, table[1:]):
+            assert e0[2] == e1[1] and e0[0] < e1[0]
+
+
+def test_clip_union_over_ranks_is_global_segmentation():
+    w = WORKLOADS["8k_p6"]
+    pieces = []
+    for a, cnt in oracle.partition(w.n_tokens, w.world):
+        for s, lo, hi in oracle.clip_segments(w.cu, a, a + cnt):
+            pieces.append((s, a + lo, a + hi))
+    merged = {}
+    for s, lo, hi in pieces:
+        merged.setdefault(s, []).append((lo, hi))
+    for s, spans in merged.items():
+        spans.sort()
+        assert spans[0][0] == w.cu[s] and spans[-1][1] == w.cu[s + 1]
+        for x, y in zip(spans, spans[1:]):
+            assert x[1] == y[0]
+    assert sorted(merged) == list(range(w.n_segments))
+
+
+# ---------------------------------------------------------------------------
+# relayouts
+# ---------------------------------------------------------------------------
+
+def _coded_qkv(n, k, h, d):
+    """int64 operand whose entry at (t, p, h, d) is the number of that position."""
+    return np.arange(n * k * h * d, dtype=np.int64).reshape(n, k, h, d)
+
+
+@pytest.mark.parametrize("world", [1, 2, 4, 6, 8])
+def test_seq2head_elements_come_from_their_owner_head(world):
+    table = {int(r): [int(x) for x in hs.split(",")] for r, hs in _read_golden("head_partition.txt")}
+    n, k, h, d = 37, 3, 56, 4        # 37 tokens: a ragged token split for every world size
+    src = _coded_qkv(n, k, h, d)
+    out = oracle.seq2head(src, world)
+    counts = table.get(world, [56])
+    starts = np.cumsum([0] + counts[:-1])
+    for j in range(world):
+        for p in range(k):
+            buf = out[(j, p)]
+            assert buf.shape == (n, counts[j], d)
+            t, hl, dd = np.meshgrid(np.arange(n), np.arange(counts[j]), np.arange(d), indexing="ij")
+            decoded_h = (buf // d) % h
+            decoded_p = (buf // (d * h)) % k
+            decoded_t = buf // (d * h * k)
+            assert np.array_equal(decoded_t, t)
+            assert np.array_equal(decoded_p, np.full_like(t, p))
+            assert np.array_equal(decoded_h, starts[j] + hl)
+            assert np.array_equal(buf % d, dd)
+            assert not np.shares_memory(buf, src)
+
+
+@pytest.mark.parametrize("world", [1, 2, 4, 6, 8])
+def test_transport_identity_round_trip(world):
+    src = normal_bf16_bits((45, 4, 56, 8), seed=11)
+    out = oracle.seq2head(src, world)
+    for p in range(4):
+        back = oracle.head2seq([out[(j, p)] for j in range(world)], 56)
+        assert back.dtype == np.uint16
+        assert np.array_equal(back, src[:, p])
+
+
+def test_world_size_one_is_a_copy():
+    src = normal_bf16_bits((19, 3, 56, 8), seed=12)
+    out = oracle.seq2head(src, 1)
+    for p in range(3):
+        assert np.array_equal(out[(0, p)], src[:, p])
+        assert not np.shares_memory(out[(0, p)], src)
+
+
+def test_head2seq_elements_land_on_their_global_head():
+    n, h, d, world = 23, 56, 4, 6
+    heads = oracle.partition(h, world)
+    bufs = []
+    for hb, hn in heads:
+        t, hl, dd = np.meshgrid(np.arange(n), np.arange(hn), np.arange(d), indexing="ij")
+        bufs.append((t * h + hb + hl) * d + dd)        # code of the global position
+    out = oracle.head2seq(bufs, h)
+    assert np.array_equal(out.reshape(-1), np.arange(n * h * d))
+
+
+def test_head2seq_rejects_wrong_buffer_shape():
+    bufs = [np.zeros((8, 28, 4), np.uint16), np.zeros((8, 27, 4), np.uint16)]
+    with pytest.raises(ValueError):
+        oracle.head2seq(bufs, 56)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _qkvg(n, h, d, seed, qscale=1.0):
+    q = normal_bf16_bits((n, h, d), seed, std=qscale)
+    k = normal_bf16_bits((n, h, d), seed + 1)
+    v = normal_bf16_bits((n, h, d), seed + 2)
+    g = normal_bf16_bits((n, h, d), seed + 3)
+    return q, k, v, g
+
+
+def _sdpa_f64(q, k, v, scale):
+    """torch's scaled-dot-product attention in float64 on the CPU, [L, H, D] operands."""
+    f = lambda a: torch.from_numpy(oracle.bf16_bits_to_f64(a)).permute(1, 0, 2).contiguous()  # noqa: E731
+    o = torch.nn.functional.scaled_dot_product_attention(f(q), f(k), f(v), scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_attention_matches_dense_brute_force(gated):
+    cu = [0, 1, 17, 64, 65, 130, 200]
+    n, h, d = 200, 3, 32
+    q, k, v, g = _qkvg(n, h, d, seed=21)
+    scale = d ** -0.5
+    got = oracle.attention_rows(q, k, v, g if gated else None, cu, scale)
+    ref = oracle.attention_dense(q, k, v, g if gated else None, cu, scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("qscale", [1.0, 8.0])
+def test_attention_segments_match_library_sdpa(qscale):
+    cu = [0, 96, 256, 300]
+    n, h, d = 300, 4, 128
+    q, k, v, g = _qkvg(n, h, d, seed=31, qscale=qscale)
+    scale = 128 ** -0.5
+    got = oracle.attention_rows(q, k, v, None, cu, scale)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        ref = _sdpa_f64(q[a:b], k[a:b], v[a:b], scale)
+        np.testing.assert_allclose(got[a:b], ref, rtol=0, atol=1e-10)
+
+
+def test_attention_gate_is_sigmoid_of_g():
+    cu = [0, 40, 100]
+    n, h, d = 100, 2, 64
+    q, k, v, g = _qkvg(n, h, d, seed=41)
+    scale = 0.125
+    got = oracle.attention_rows(q, k, v, g, cu, scale)
+    ungated = oracle.attention_rows(q, k, v, None, cu, scale)
+    sig = torch.sigmoid(torch.from_numpy(oracle.bf16_bits_to_f64(g))).numpy()
+    np.testing.assert_allclose(got, ungated * sig, rtol=1e-13, atol=0)
+    # G = 0 halves the output exactly
+    half = oracle.attention_rows(q, k, v, np.zeros_like(g), cu, scale)
+    assert np.array_equal(half, ungated * 0.5)
+
+
+def test_attention_closed_forms():
+    n, h, d = 48, 2, 16
+    q, k, v, g = _qkvg(n, h, d, seed=51)
+    cu = [0, 1, 20, 48]
+    # a one-token segment returns its own value row exactly
+    o = oracle.attention_rows(q, k, v, None, cu, 0.3, rows=[0])
+    assert np.array_equal(o[0], oracle.bf16_bits_to_f64(v[0]))
+    # a value row that is constant over a segment comes back for every query of it
+    v2 = v.copy()
+    v2[1:20] = v2[1]
+    o = oracle.attention_rows(q, k, v2, None, cu, 0.3)
+    np.testing.assert_allclose(o[1:20], np.broadcast_to(oracle.bf16_bits_to_f64(v2[1]), (19, h, d)),
+                               rtol=0, atol=1e-12)
+    # identical key rows make the weights uniform: the segment mean of V
+    k2 = k.copy()
+    k2[20:48] = k2[20]
+    o = oracle.attention_rows(q, k2, v, None, cu, 0.3)
+    mean = oracle.bf16_bits_to_f64(v[20:48]).mean(axis=0)
+    np.testing.assert_allclose(o[20:48], np.broadcast_to(mean, (28, h, d)), rtol=0, atol=1e-12)
+
+
+def test_attention_key_permutation_inside_segment():
+    n, h, d = 64, 2, 16
+    q, k, v, _ = _qkvg(n, h, d, seed=61)
+    cu = [0, 30, 64]
+    perm = np.arange(n)
+    perm[30:64] = 30 + np.random.default_rng(3).permutation(34)
+    o1 = oracle.attention_rows(q, k, v, None, cu, 0.25)
+    o2 = oracle.attention_rows(q, k[perm], v[perm], None, cu, 0.25)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    # moving a key across the boundary DOES change the result (segments do not mix)
+    swap = np.arange(n)
+    swap[29], swap[30] = 30, 29
+    o3 = oracle.attention_rows(q, k[swap], v[swap], None, cu, 0.25)
+    assert np.abs(o3 - o1).max() > 1e-3
+
+
+def test_attention_row_subset_equals_full():
+    n, h, d = 90, 2, 32
+    q, k, v, g = _qkvg(n, h, d, seed=71)
+    cu = [0, 33, 90]
+    full = oracle.attention_rows(q, k, v, g, cu, 0.2)
+    rows = [89, 0, 33, 32, 50]
+    sub = oracle.attention_rows(q, k, v, g, cu, 0.2, rows=rows, threads=3)
+    assert np.array_equal(sub, full[rows])
+
+
+def test_attention_flops_closed_form():
+    w = WORKLOADS["128k_p4_qkvg"]
+    assert oracle.attention_flops(w.cu, 14, 128) == 4 * 128 * 14 * (98304 ** 2 + 32768 ** 2)
+
+
+# ---------------------------------------------------------------------------
+# AdaLN
+# ---------------------------------------------------------------------------
+
+def _adaln_inputs(n, c, s, seed):
+    x = normal_bf16_bits((n, c), seed)
+    b = normal_bf16_bits((n, c), seed + 1)
+    shift = normal_bf16_bits((s, c), seed + 2, std=0.1)
+    scale = normal_bf16_bits((s, c), seed + 3, std=0.1)
+    gate = normal_bf16_bits((s, c), seed + 4, std=0.1)
+    return x, b, shift, scale, gate
+
+
+def _segment_of_token(cu, t):
+    return max(i for i in range(len(cu) - 1) if cu[i] <= t)
+
+
+def test_adaln_modulate_matches_library_layer_norm():
+    cu = [0, 96, 256, 512]
+    n, c = 512, 256
+    x, b, shift, scale, gate = _adaln_inputs(n, c, 3, seed=81)
+    eps = 1e-6
+    for a, e in [(0, 512), (0, 256), (256, 512), (100, 300)]:
+        got = oracle.adaln_rows(oracle.MODULATE, x[a:e], None, shift, scale, None, a, e, cu, eps)
+        xf = torch.from_numpy(oracle.bf16_bits_to_f64(x[a:e]))
+        ln = torch.nn.functional.layer_norm(xf, (c,), eps=eps).numpy()
+        seg = np.array([_segment_of_token(cu, t) for t in range(a, e)])
+        ref = ln * (1.0 + oracle.bf16_bits_to_f64(scale)[seg]) + oracle.bf16_bits_to_f64(shift)[seg]
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_adaln_modulate_closed_forms():
+    cu = [0, 5, 12]
+    n, c = 12, 64
+    x, b, shift, scale, gate = _adaln_inputs(n, c, 2, seed=91)
+    zero = np.zeros_like(shift)
+    y = oracle.adaln_rows(oracle.MODULATE, x, None, zero, zero, None, 0, n, cu, 0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, atol=1e-12)
+    # a constant row normalises to zero, leaving exactly the shift of its global segment
+    xc = np.broadcast_to(x[:, :1], x.shape).copy()
+    y = oracle.adaln_rows(oracle.MODULATE, xc, None, shift, scale, None, 0, n, cu, 1e-6)
+    sh = oracle.bf16_bits_to_f64(shift)
+    assert np.array_equal(y[:5], np.broadcast_to(sh[0], (5, c)))
+    assert np.array_equal(y[5:], np.broadcast_to(sh[1], (7, c)))
+
+
+def test_adaln_gate_closed_forms():
+    cu = [0, 7, 20, 33]
+    n, c = 33, 32
+    x, b, shift, scale, gate = _adaln_inputs(n, c, 3, seed=101)
+    # zero gate: residual passes unchanged
+    y = oracle.adaln_rows(oracle.GATE_RESIDUAL, x, b, None, None, np.zeros_like(gate), 0, n, cu, 0.0)
+    assert np.array_equal(y, oracle.bf16_bits_to_f64(x))
+    # unit branch: y - x is the gate row of the token's global segment
+    one = np.full_like(b, 0x3F80)      # bf16 bits of 1.0
+    a, e = 5, 30                       # an interval that cuts segments 0 and 2
+    y = oracle.adaln_rows(oracle.GATE_RESIDUAL, x[a:e], one[a:e], None, None, gate, a, e, cu, 0.0)
+    gf = oracle.bf16_bits_to_f64(gate)
+    for t in range(a, e):
+        assert np.array_equal(y[t - a] - oracle.bf16_bits_to_f64(x[t]), gf[_segment_of_token(cu, t)])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_adaln_per_rank_equals_global(mode):
+    w = WORKLOADS["8k_p6"]
+    n, c = w.n_tokens, 64
+    x, b, shift, scale, gate = _adaln_inputs(n, c, w.n_segments, seed=111)
+    whole = oracle.adaln_rows(mode, x, b, shift, scale, gate, 0, n, w.cu, 1e-6)
+    for a, cnt in oracle.partition(n, w.world):
+        part = oracle.adaln_rows(mode, x[a:a + cnt], b[a:a + cnt], shift, scale, gate, a, a + cnt,
+                                 w.cu, 1e-6)
+        assert np.array_equal(part, whole[a:a + cnt])
