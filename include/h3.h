@@ -1,0 +1,206 @@
+/*
+ * h3.h -- C ABI of the MI355X (gfx950) Ulysses H3 hot-path library, libh3.so.
+ *
+ * The library implements, for ONE GPU, the data-parallel hot path of a
+ * Ulysses sequence-parallel H3 denoiser block: the sequence-to-head relayout
+ * of packed QKV/QKVG, segment-masked attention over the natively packed
+ * multi-segment sequence, the inverse head-to-sequence relayout, and the
+ * per-segment AdaLN modulation / residual gating on segment tables clipped to
+ * a token interval.  The P ranks of the sequence-parallel group are emulated
+ * by P "virtual-rank" buffers on the one device; no collective is issued.
+ *
+ * Sources (by page title and section):
+ *   [DIST]  "Distributed H3 Execution" -- introduction, Partition Contract,
+ *           Validation.
+ *   [PR]    "[perf] Harden Ulysses agreement and tune bounded H3 transfers"
+ *           -- Problem and behavior, Implementation.
+ *   [SPARK] "MiniMax H3 on NVIDIA DGX Spark (GB10)" -- Choosing the
+ *           encoder-node count (only its error style: list the legal values).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - Element type: every tensor is bfloat16, row-major, densely packed.
+ * - Pointers: "device" pointers are HIP device memory owned by the caller;
+ *   "host" pointers are ordinary host memory read only during the call.
+ *   The library never allocates, frees or synchronises; work is enqueued on
+ *   `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *   runs asynchronously.  Buffers must stay alive until that work completes.
+ * - Independent storage ([PR], Problem and behavior): no output may overlap
+ *   an input or another output; overlap is detected on the host from the
+ *   address ranges and rejected with H3_ERR_ALIAS.
+ * - Validation first: every check runs on the host before anything is
+ *   enqueued.  On any error nothing is launched, no state is kept, and the
+ *   next valid call behaves as if the failed one never happened (the local
+ *   form of [PR], Implementation: a declined call can recover on a later
+ *   compatible call).  h3_last_error() returns a message for the calling
+ *   thread's last failure.
+ * - Empty partitions are rejected ([DIST], introduction): a split that would
+ *   leave some rank without heads or tokens returns H3_ERR_EMPTY_PARTITION
+ *   and the message lists the legal rank counts ([SPARK] style).
+ * - h3_plan_info, when non-NULL, receives what was actually enqueued, so a
+ *   caller can assert the execution plan and not just the numbers.
+ * - Thread safety: all entry points are stateless and may be called from
+ *   several threads; the per-thread error text is thread-local.
+ */
+#ifndef H3_H
+#define H3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum h3_status {
+    H3_OK = 0,
+    H3_ERR_ARG = 1,              /* NULL pointer, negative or inconsistent size, bad mode       */
+    H3_ERR_EMPTY_PARTITION = 2,  /* P < 1, or P larger than the heads or tokens to split       */
+    H3_ERR_SEGMENTS = 3,         /* segment table not 0 = cu[0] < ... < cu[S] = N, or S too big */
+    H3_ERR_UNSUPPORTED = 4,      /* head_dim != 128, channels not a multiple of 8 or too large */
+    H3_ERR_ALIAS = 5,            /* an output overlaps an input or another output              */
+    H3_ERR_HIP = 6               /* the HIP runtime refused a launch                           */
+} h3_status;
+
+#define H3_HEAD_DIM 128          /* the only supported head width (56 heads of width 128, [DIST]) */
+#define H3_MAX_SEGMENTS 256      /* largest segment table accepted                            */
+#define H3_MAX_HEADS 256         /* largest head count accepted                               */
+#define H3_MAX_CHANNELS 16384    /* largest AdaLN row width accepted                          */
+
+/* The per-call relayout contract (cf. [PR], Implementation: the call contract
+ * carries the chunking and launch size). */
+typedef struct h3_layout {
+    int64_t n_tokens;        /* N: packed tokens over all segments, >= 1                      */
+    int32_t n_heads;         /* H: global heads (56 for H3), 1..H3_MAX_HEADS                  */
+    int32_t head_dim;        /* D: must be H3_HEAD_DIM                                        */
+    int32_t n_planes;        /* K: planes in the packed operand (3 = QKV, 4 = QKVG); 1 for
+                                head2seq                                                      */
+    int32_t world;           /* P: virtual ranks, 1 <= P <= min(H, N)                          */
+    int32_t rank;            /* -1: every rank; 0..P-1: only that rank's share                */
+    int32_t reserved;        /* must be 0                                                     */
+    int64_t max_chunk_bytes; /* 0: one launch per plane; > 0: each launch covers at most
+                                floor(max_chunk_bytes / (H*D*2)) tokens of one plane (the
+                                896,000,000-byte window of [PR] gives 62,500 tokens)          */
+} h3_layout;
+
+typedef struct h3_plan_info {
+    int32_t launches;        /* kernel launches enqueued by the call                          */
+    int32_t chunks;          /* token chunks per plane (relayouts), 1 otherwise               */
+    int32_t grid_x;          /* workgroups of the largest launch                              */
+    int32_t block_x;         /* threads per workgroup                                         */
+    int64_t chunk_tokens;    /* tokens per full chunk (relayouts)                             */
+    int64_t max_launch_src_bytes; /* most source bytes read by one launch                     */
+    int64_t bytes_read;      /* algorithmic bytes read by the whole call                      */
+    int64_t bytes_written;   /* algorithmic bytes written by the whole call                   */
+    double flops;            /* attention: algorithmic FLOPs (4*D per query-key pair per head) */
+    int64_t tiles;           /* attention: query tiles x heads; AdaLN: clipped table entries   */
+} h3_plan_info;
+
+/* ------------------------------------------------------------------------
+ * h3_seq2head -- sequence-to-head relayout, one plane at a time.
+ *
+ * [DIST] introduction: Ulysses mode wraps attention in a QKV sequence-to-head
+ * all-to-all; [DIST] Partition Contract: rank j owns heads [hb_j, hb_j+H_j)
+ * of the balanced quotient/remainder split (10,10,9,9,9,9 for 56 over 6) and
+ * tokens [a_j, b_j) of the same split of N; [PR] Problem and behavior: one
+ * batch plane at a time, bounded windows, outputs in storage of their own.
+ *
+ * src: device, [N][K][H][D], the packed operand (token-major, planes Q,K,V[,G]).
+ * dst: host array of P*K device pointers; dst[j*K + p] is rank j's buffer of
+ *      plane p, [N][H_j][D] (every token of rank j's heads, global token
+ *      order -- what the all-to-all leaves on rank j).  When layout->rank = j
+ *      only the K entries of rank j are read; the others may be NULL.
+ * Effect: dst[j*K+p][t][h][:] = src[t][p][hb_j + h][:], bit for bit.
+ * Launches: K * chunks (one per plane and token chunk), in plane order.
+ * ------------------------------------------------------------------------ */
+h3_status h3_seq2head(const h3_layout *layout, const void *src, void *const *dst,
+                      void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_head2seq -- the inverse, head-to-sequence relayout ([DIST] introduction).
+ *
+ * src: host array of P device pointers; src[j] is rank j's [N][H_j][D] buffer
+ *      (e.g. the attention output of its heads).  With layout->rank = j only
+ *      src[j] is read.
+ * dst: device, [N][H][D].  Effect: dst[t][hb_j + h][:] = src[j][t][h][:] for
+ *      every selected rank j; heads of unselected ranks are left untouched.
+ * layout->n_planes must be 1.  Launches: chunks (one per token chunk).
+ * ------------------------------------------------------------------------ */
+h3_status h3_head2seq(const h3_layout *layout, const void *const *src, void *dst,
+                      void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_packed_attn -- segment-masked attention over the packed sequence, for
+ * the heads one rank holds after seq2head ([DIST] introduction: attention on
+ * the whole native packed sequence, no semantic padding).
+ *
+ * For every head h and token t in segment s = [cu[s], cu[s+1]):
+ *   o[t,h,:] = sum_{u in s} softmax_u(scale * <q[t,h,:], k[u,h,:]>) v[u,h,:]
+ * and, when g != NULL (QKVG, [PR] Problem and behavior), o[t,h,:] *= 1/(1+exp(-g[t,h,:])).
+ * Tokens never attend across a segment boundary; no work is spent on the
+ * cross-segment blocks.  bf16 inputs, fp32 accumulation, bf16 output
+ * (round to nearest even).
+ *
+ * q, k, v, g, o: device, [N][n_heads][D] each (g may be NULL).
+ * cu_seqlens: host, S+1 int64 offsets, 0 = cu[0] < cu[1] < ... < cu[S] = N,
+ *             1 <= S <= H3_MAX_SEGMENTS.
+ * scale: logit scale (1/sqrt(128) for H3).  Launches: 1.
+ * ------------------------------------------------------------------------ */
+h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void *g, void *o,
+                         int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                         const int64_t *cu_seqlens, int32_t n_segments, float scale,
+                         void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_adaln_segment -- per-segment AdaLN on one rank's token interval.
+ *
+ * [DIST] Partition Contract: segment boundaries are clipped to the rank's
+ * token interval [tok_begin, tok_end) and rebased before AdaLN modulation
+ * and residual gating.  Local row i is global token tok_begin + i and takes
+ * the parameter row of its GLOBAL segment s.
+ *   mode H3_ADALN_MODULATE:      y = (x - mean)/sqrt(var + eps) * (1 + scale[s]) + shift[s]
+ *                                 (mean and biased var over the C channels, fp32)
+ *   mode H3_ADALN_GATE_RESIDUAL: y = x + gate[s] * branch
+ *
+ * x, branch, y: device, [tok_end - tok_begin][C].  branch only for GATE.
+ * shift, scale (MODULATE) / gate (GATE): device, [S][C].
+ * cu_seqlens: host, the GLOBAL table (S+1 offsets, cu[S] >= tok_end).
+ * channels: C, a multiple of 8, <= H3_MAX_CHANNELS.  Launches: 1.
+ * ------------------------------------------------------------------------ */
+#define H3_ADALN_MODULATE 0
+#define H3_ADALN_GATE_RESIDUAL 1
+h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift,
+                           const void *scale, const void *gate, void *y,
+                           int64_t tok_begin, int64_t tok_end, int32_t channels,
+                           const int64_t *cu_seqlens, int32_t n_segments, float eps,
+                           void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * Host-only helpers (no device work, callable without a GPU).
+ * ------------------------------------------------------------------------ */
+
+/* [DIST] Partition Contract: part `index` of `total` items split over
+ * `parts` ranks, first (total mod parts) ranks one larger.  Writes its first
+ * item and size.  H3_ERR_EMPTY_PARTITION if parts < 1 or parts > total. */
+h3_status h3_partition(int64_t total, int32_t parts, int32_t index, int64_t *begin, int64_t *count);
+
+/* [DIST] Partition Contract: clip the global table cu[0..S] to [a, b) and
+ * rebase.  Writes up to S entries (global segment id, local begin, local
+ * end) of the non-empty pieces, in order.  Returns the entry count, or -1 if
+ * the table or the interval is invalid.  Output arrays may be NULL to count. */
+int32_t h3_clip_segments(const int64_t *cu, int32_t n_segments, int64_t a, int64_t b,
+                         int32_t *seg_id, int64_t *local_begin, int64_t *local_end);
+
+/* Static text for a status code. */
+const char *h3_status_string(h3_status status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *h3_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *h3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3_H */

@@ -34,6 +34,7 @@ class Workload:
     cu: Tuple[int, ...]        # global segment offsets
     seed: int
     attn_rank: Optional[int]   # None: attention for every rank's heads; j: only rank j's share
+    relayout_rank: int = -1    # -1: relayout into every rank's buffers; j: only rank j's share
     max_chunk_bytes: int = 0   # 0: one launch per plane; else source-byte cap per launch
     description: str = ""
 
@@ -71,13 +72,13 @@ WORKLOADS = {
                     "virtual-rank buffers, attention over one rank's 14 heads, head2seq"),
     "128k_p4_qkvg": Workload(
         name="128k_p4_qkvg", n_tokens=131072, world=4, planes=4,
-        cu=segment_offsets([98304, 32768]), seed=1004, attn_rank=0,
+        cu=segment_offsets([98304, 32768]), seed=1004, attn_rank=0, relayout_rank=0,
         description="131072 packed tokens, QKVG [131072,4,56,128], segments 98304+32768, P=4, "
                     "rank share (14 heads), plane-at-a-time relayout, gated attention, "
                     "head2seq, AdaLN modulation on [131072,7168]"),
     "250k_p8_qkvg": Workload(
         name="250k_p8_qkvg", n_tokens=250000, world=8, planes=4,
-        cu=tuple(_random_cuts(250000, 8, 1005)), seed=1005, attn_rank=0,
+        cu=tuple(_random_cuts(250000, 8, 1005)), seed=1005, attn_rank=0, relayout_rank=0,
         max_chunk_bytes=896_000_000,
         description="250000 packed tokens, 8 seeded random segments, P=8 (7 heads), QKVG "
                     "relayout in launches of at most 896,000,000 source bytes, gated attention, "

@@ -1,0 +1,138 @@
+"""GPU parity of segment-masked packed attention against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, segment_offsets
+from synth.inputs import normal_bf16, normal_bf16_bits
+from tests.gpu_util import compare, say, sample_rows, to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+SCALE = 128 ** -0.5
+
+
+def _h3():
+    import ulysses_layout_amd as h3
+    return h3
+
+
+def _run(q, k, v, g, cu):
+    h3 = _h3()
+    o = torch.empty_like(q)
+    info = h3.packed_attn(q, k, v, g, o, cu, SCALE)
+    torch.cuda.synchronize()
+    return o, info
+
+
+RAGGED = [
+    [1],
+    [64],
+    [1, 63, 64, 65],
+    [127, 128, 129],
+    [300],
+    [5, 250, 1, 77, 130],
+    [96, 160, 256],
+]
+
+
+@pytest.mark.parametrize("lengths", RAGGED, ids=lambda x: "-".join(map(str, x)))
+@pytest.mark.parametrize("gated", [False, True])
+def test_attention_ragged_segments(lengths, gated):
+    cu = segment_offsets(lengths)
+    n, h = cu[-1], 3
+    say("attention ragged", lengths, gated)
+    bits = [normal_bf16_bits((n, h, 128), seed=400 + i + n) for i in range(4)]
+    q, k, v, g = (to_device(b) for b in bits)
+    o, info = _run(q, k, v, g if gated else None, cu)
+    ref = oracle.attention_rows(bits[0], bits[1], bits[2], bits[3] if gated else None, cu, SCALE)
+    compare(to_bits(o), ref, f"attn {lengths} gated={gated}")
+    assert info.launches == 1
+    assert info.flops == 4 * 128 * h * sum(L * L for L in lengths)
+
+
+def test_attention_peaky_softmax():
+    """Q scaled by 8: large logits exercise the online-softmax rescaling."""
+    cu = segment_offsets([700, 333])
+    n, h = cu[-1], 2
+    say("attention peaky")
+    q_bits = normal_bf16_bits((n, h, 128), seed=501, std=8.0)
+    k_bits, v_bits = normal_bf16_bits((n, h, 128), seed=502), normal_bf16_bits((n, h, 128), seed=503)
+    o, _ = _run(to_device(q_bits), to_device(k_bits), to_device(v_bits), None, cu)
+    compare(to_bits(o), oracle.attention_rows(q_bits, k_bits, v_bits, None, cu, SCALE), "attn peaky")
+
+
+def test_attention_gate_zero_halves_exactly():
+    cu = segment_offsets([200, 57])
+    n, h = cu[-1], 2
+    say("attention G=0")
+    q, k, v = (normal_bf16((n, h, 128), seed=600 + i, device="cuda") for i in range(3))
+    o, _ = _run(q, k, v, None, cu)
+    og, _ = _run(q, k, v, torch.zeros_like(q), cu)
+    assert torch.equal(og.float() * 2, o.float())
+
+
+def test_attention_segments_do_not_mix():
+    """Changing one segment's keys and values leaves every other segment's output bits unchanged."""
+    cu = segment_offsets([130, 200, 70])
+    n, h = cu[-1], 2
+    say("attention isolation")
+    q, k, v = (normal_bf16((n, h, 128), seed=700 + i, device="cuda") for i in range(3))
+    o1, _ = _run(q, k, v, None, cu)
+    k2, v2 = k.clone(), v.clone()
+    k2[130:330] = normal_bf16((200, h, 128), seed=711, device="cuda")
+    v2[130:330] = normal_bf16((200, h, 128), seed=712, device="cuda")
+    o2, _ = _run(q, k2, v2, None, cu)
+    assert torch.equal(o1[:130].view(torch.int16), o2[:130].view(torch.int16))
+    assert torch.equal(o1[330:].view(torch.int16), o2[330:].view(torch.int16))
+    assert not torch.equal(o1[130:330].view(torch.int16), o2[130:330].view(torch.int16))
+
+
+def test_attention_deterministic():
+    cu = segment_offsets([1000, 24])
+    n, h = cu[-1], 4
+    q, k, v, g = (normal_bf16((n, h, 128), seed=800 + i, device="cuda") for i in range(4))
+    o1, _ = _run(q, k, v, g, cu)
+    o2, _ = _run(q, k, v, g, cu)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny512", "8k_p6"])
+def test_attention_workload_every_row(name):
+    """Small workloads: every rank's heads, every row, element by element."""
+    h3 = _h3()
+    w = WORKLOADS[name]
+    say("attention workload full", name)
+    src = normal_bf16((w.n_tokens, w.planes, 56, 128), seed=w.seed, device="cuda")
+    src_bits = to_bits(src)
+    heads = h3.head_split(56, w.world)
+    for j, (_, c) in enumerate(heads):
+        ref_in = oracle.seq2head(src_bits, w.world, ranks=[j])
+        q, k, v = (to_device(ref_in[(j, p)]) for p in range(3))
+        o, _ = _run(q, k, v, None, w.cu)
+        ref = oracle.attention_rows(ref_in[(j, 0)], ref_in[(j, 1)], ref_in[(j, 2)], None, w.cu, SCALE)
+        compare(to_bits(o), ref, f"{name} rank {j}")
+
+
+@pytest.mark.parametrize("name", ["32k_p4", "128k_p4_qkvg", "250k_p8_qkvg"])
+def test_attention_workload_sampled_rows(name):
+    """Large workloads at full size, in the launch configuration of the bench:
+    one rank's heads over the whole packed sequence, checked on sampled rows."""
+    h3 = _h3()
+    w = WORKLOADS[name]
+    j = w.attn_rank
+    say("attention workload sampled", name, "rank", j)
+    heads = h3.head_split(56, w.world)
+    n, c = w.n_tokens, heads[j][1]
+    ops = [normal_bf16((n, c, 128), seed=w.seed + 10 + p, device="cuda") for p in range(w.planes)]
+    g = ops[3] if w.planes >= 4 else None
+    o, info = _run(ops[0], ops[1], ops[2], g, w.cu)
+    bounds = [a for a, _ in (h3.partition(n, w.world, i) for i in range(w.world))]
+    rows = sample_rows(w.cu, seed=w.seed, per_tile=2048, boundaries=bounds, limit=160)
+    bits = [to_bits(t) for t in ops]
+    ref = oracle.attention_rows(bits[0], bits[1], bits[2], bits[3] if g is not None else None, w.cu, SCALE,
+                                rows=rows)
+    got = to_bits(o)[rows]
+    compare(got, ref, f"{name} sampled {len(rows)} rows")
+    expected_flops = 4 * 128 * c * sum(L * L for L in w.segment_lengths)
+    assert info.flops == expected_flops

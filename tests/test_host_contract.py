@@ -1,0 +1,203 @@
+"""Host-side contract of libh3.so, runnable without a GPU.
+
+* the library loads and exports every function include/h3.h declares;
+* the host helpers (partition, clip) equal the oracle exactly;
+* every invalid call is rejected on the host with the documented status, before
+  anything could be enqueued (fake device addresses are never dereferenced),
+  and a rejected call leaves nothing behind for the next one.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import ulysses_layout_amd as h3
+from ulysses_layout_amd.h3 import Layout, _PlanInfo
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3.h")
+
+ARG, EMPTY, SEGS, UNSUP, ALIAS = 1, 2, 3, 4, 5
+FAKE = 1 << 40     # a device-looking address that is never touched
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"h3_seq2head", "h3_head2seq", "h3_packed_attn", "h3_adaln_segment"}
+    lib = ctypes.CDLL(h3.h3.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), f"libh3.so does not export {name}"
+    assert set(names) == set(h3.EXPORTS)
+
+
+def test_library_is_built_for_gfx950():
+    blob = open(h3.h3.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_partition_equals_oracle():
+    for total in list(range(1, 40)) + [56, 8192, 131072, 250000]:
+        for parts in range(1, min(total, 64) + 1):
+            ref = oracle.partition(total, parts)
+            for j in range(parts):
+                assert h3.partition(total, parts, j) == ref[j]
+
+
+@pytest.mark.parametrize("total,parts", [(56, 0), (56, 57), (5, 6), (0, 1)])
+def test_partition_rejects_empty(total, parts):
+    with pytest.raises(h3.H3Error) as e:
+        h3.partition(total, parts, 0)
+    assert e.value.status == EMPTY
+    assert "legal" in e.value.message
+
+
+def test_clip_equals_oracle():
+    rng = np.random.default_rng(5)
+    for w in WORKLOADS.values():
+        for a, cnt in oracle.partition(w.n_tokens, w.world):
+            assert h3.clip_segments(w.cu, a, a + cnt) == oracle.clip_segments(w.cu, a, a + cnt)
+    for _ in range(300):
+        n = int(rng.integers(2, 500))
+        s = int(rng.integers(1, min(n, 30) + 1))
+        cu = [0] + sorted(int(c) for c in rng.choice(np.arange(1, n), size=s - 1, replace=False)) + [n]
+        a = int(rng.integers(0, n))
+        b = int(rng.integers(a + 1, n + 1))
+        assert h3.clip_segments(cu, a, b) == oracle.clip_segments(cu, a, b)
+
+
+def test_clip_rejects_bad_input():
+    with pytest.raises(h3.H3Error):
+        h3.clip_segments([0, 5, 5, 9], 0, 9)      # empty segment
+    with pytest.raises(h3.H3Error):
+        h3.clip_segments([0, 5, 9], 3, 3)         # empty interval
+    with pytest.raises(h3.H3Error):
+        h3.clip_segments([0, 5, 9], 3, 10)        # past the end
+
+
+# ---------------------------------------------------------------------------
+# validation of the device entry points, straight through the C ABI
+# ---------------------------------------------------------------------------
+
+LIB = h3.library()
+
+
+def _seq2head(layout, src=FAKE, dst=None):
+    k, p = layout.n_planes, layout.world
+    if dst is None:
+        heads = [c for _, c in oracle.partition(layout.n_heads, p)] if 1 <= p <= layout.n_heads else []
+        dst, addr = [], FAKE * 2
+        for j in range(max(p, 0)):
+            for _ in range(k):
+                dst.append(addr)
+                addr += layout.n_tokens * (heads[j] if heads else 1) * 256 + 4096
+    arr = (ctypes.c_void_p * max(len(dst), 1))(*dst)
+    info = _PlanInfo()
+    return LIB.h3_seq2head(ctypes.byref(layout), src, arr, None, ctypes.byref(info)), info
+
+
+def _layout(**kw):
+    base = dict(n_tokens=512, n_heads=56, head_dim=128, n_planes=3, world=2, rank=-1, reserved=0,
+                max_chunk_bytes=0)
+    base.update(kw)
+    return Layout(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(world=0), EMPTY), (dict(world=57), EMPTY), (dict(n_tokens=3, world=4), EMPTY),
+    (dict(n_tokens=0), EMPTY), (dict(head_dim=64), UNSUP), (dict(n_planes=0), ARG),
+    (dict(n_planes=9), ARG), (dict(rank=2), ARG), (dict(rank=-2), ARG), (dict(reserved=1), ARG),
+    (dict(max_chunk_bytes=-1), ARG), (dict(max_chunk_bytes=1000), ARG), (dict(n_heads=0), ARG),
+])
+def test_seq2head_rejects_bad_layout(kw, status):
+    rc, info = _seq2head(_layout(**kw))
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+    msg = LIB.h3_last_error().decode()
+    assert msg
+    if status == EMPTY and "world" in kw:
+        assert "legal values are 1.." in msg
+
+
+def test_seq2head_rejects_null_and_alias():
+    lay = _layout()
+    rc, _ = _seq2head(lay, src=None)
+    assert rc == ARG
+    # one destination placed inside the source
+    src_bytes = 512 * 3 * 56 * 128 * 2
+    dst = [FAKE * 2 + i * (1 << 24) for i in range(6)]
+    dst[3] = FAKE + src_bytes // 2
+    rc, _ = _seq2head(lay, dst=dst)
+    assert rc == ALIAS
+    # two destinations overlapping each other
+    dst = [FAKE * 2 + i * (1 << 24) for i in range(6)]
+    dst[4] = dst[1] + 256
+    rc, _ = _seq2head(lay, dst=dst)
+    assert rc == ALIAS
+    dst = [FAKE * 2 + i * (1 << 24) for i in range(6)]
+    dst[5] = None
+    rc, _ = _seq2head(lay, dst=dst)
+    assert rc == ARG
+
+
+def test_rejected_call_leaves_no_state():
+    rc, _ = _seq2head(_layout(world=57))
+    assert rc == EMPTY
+    assert h3.partition(56, 6, 0) == (0, 10)           # next valid call works
+    assert LIB.h3_last_error().decode() == ""
+
+
+def _attn(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), g=None, o=FAKE + (3 << 32), n=512, h=4, d=128,
+          cu=(0, 96, 256, 512), scale=0.088):
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_packed_attn(q, k, v, g, o, n, h, d, cua, len(cu) - 1, scale, None, ctypes.byref(info))
+    return rc, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ARG), (dict(o=None), ARG), (dict(d=64), UNSUP), (dict(h=0), EMPTY), (dict(n=0), EMPTY),
+    (dict(cu=(0, 96, 96, 512)), SEGS), (dict(cu=(1, 96, 512)), SEGS), (dict(cu=(0, 96, 500)), SEGS),
+    (dict(scale=0.0), ARG), (dict(scale=float("nan")), ARG), (dict(o=FAKE + 100), ALIAS),
+    (dict(g=FAKE + (3 << 32) + 64), ALIAS), (dict(cu=tuple(range(0, 2 * 300, 2)) + (600,), n=600), SEGS),
+])
+def test_packed_attn_rejects(kw, status):
+    rc, info = _attn(**kw)
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+def _adaln(mode=0, x=FAKE, b=None, shift=FAKE + (1 << 32), scale=FAKE + (2 << 32), gate=None,
+           y=FAKE + (3 << 32), a=0, e=256, c=7168, cu=(0, 96, 256, 512), eps=1e-6):
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_adaln_segment(mode, x, b, shift, scale, gate, y, a, e, c, cua, len(cu) - 1, eps, None,
+                              ctypes.byref(info))
+    return rc, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=2), ARG), (dict(x=None), ARG), (dict(shift=None), ARG), (dict(mode=1), ARG),
+    (dict(a=10, e=10), EMPTY), (dict(a=-1), EMPTY), (dict(c=7170), UNSUP), (dict(c=0), UNSUP),
+    (dict(c=16392), UNSUP), (dict(e=600), SEGS), (dict(cu=(0, 300, 200, 512)), SEGS),
+    (dict(y=FAKE + 1000), ALIAS), (dict(eps=float("nan")), ARG),
+])
+def test_adaln_rejects(kw, status):
+    rc, info = _adaln(**kw)
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+def test_status_strings():
+    for code, name in h3.h3.STATUS_NAMES.items():
+        LIB.h3_status_string.restype = ctypes.c_char_p
+        assert LIB.h3_status_string(code).decode() == name

@@ -1,0 +1,11 @@
+"""MI355X-native Ulysses H3 hot path: seq2head / packed attention / head2seq / AdaLN.
+
+The compute lives in ``libh3.so`` (hand-written HIP for gfx950, C ABI declared
+in ``include/h3.h``); this package is its thin ctypes binding.  Importing it
+fails if the library has not been built.
+"""
+from .h3 import (  # noqa: F401
+    EXPORTS, H3_ADALN_GATE_RESIDUAL, H3_ADALN_MODULATE, HEAD_DIM, H3Error, Layout, PlanInfo,
+    adaln_segment, clip_segments, head2seq, head_split, library, packed_attn, partition, seq2head,
+    version,
+)

@@ -1,0 +1,476 @@
+// h3_api.hip -- the C ABI of libh3.so: argument validation, the launch plan
+// and the plan report.  Every check runs before anything is enqueued; a
+// rejected call leaves no state behind.  See include/h3.h for the contract.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "h3_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+h3_status fail(h3_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+h3_status ok() {
+    g_last_error[0] = '\0';
+    return H3_OK;
+}
+
+// Balanced quotient/remainder split ("Distributed H3 Execution", Partition
+// Contract): the first total%parts parts hold one extra item.
+void split(int64_t total, int32_t parts, int32_t index, int64_t *begin, int64_t *count) {
+    const int64_t q = total / parts, r = total % parts;
+    *count = q + (index < r ? 1 : 0);
+    *begin = (int64_t)index * q + std::min<int64_t>(index, r);
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    const char *what;
+    int index;
+};
+
+// Reject any output range that overlaps an input range or another output.
+h3_status check_alias(const std::vector<Range> &inputs, const std::vector<Range> &outputs) {
+    for (size_t i = 0; i < outputs.size(); ++i) {
+        const Range &o = outputs[i];
+        if (o.hi <= o.lo) continue;
+        for (const Range &in : inputs) {
+            if (in.hi > in.lo && o.lo < in.hi && in.lo < o.hi)
+                return fail(H3_ERR_ALIAS, "output %s[%d] overlaps input %s[%d]; outputs need storage of "
+                            "their own", o.what, o.index, in.what, in.index);
+        }
+        for (size_t j = i + 1; j < outputs.size(); ++j) {
+            const Range &p = outputs[j];
+            if (p.hi > p.lo && o.lo < p.hi && p.lo < o.hi)
+                return fail(H3_ERR_ALIAS, "outputs %s[%d] and %s[%d] overlap", o.what, o.index, p.what,
+                            p.index);
+        }
+    }
+    return H3_OK;
+}
+
+Range range_of(const void *p, uint64_t bytes, const char *what, int index) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes, what, index};
+}
+
+h3_status check_segments(const int64_t *cu, int32_t n_segments, int64_t n_tokens, bool exact_end) {
+    if (!cu) return fail(H3_ERR_ARG, "cu_seqlens is NULL");
+    if (n_segments < 1 || n_segments > H3_MAX_SEGMENTS)
+        return fail(H3_ERR_SEGMENTS, "n_segments = %d; legal values are 1..%d", n_segments, H3_MAX_SEGMENTS);
+    if (cu[0] != 0) return fail(H3_ERR_SEGMENTS, "cu_seqlens[0] = %lld, must be 0", (long long)cu[0]);
+    for (int32_t s = 0; s < n_segments; ++s)
+        if (cu[s + 1] <= cu[s])
+            return fail(H3_ERR_SEGMENTS, "segment %d is empty or reversed (cu[%d] = %lld, cu[%d] = %lld)", s, s,
+                        (long long)cu[s], s + 1, (long long)cu[s + 1]);
+    if (exact_end ? cu[n_segments] != n_tokens : cu[n_segments] < n_tokens)
+        return fail(H3_ERR_SEGMENTS, "cu_seqlens[%d] = %lld does not cover the %lld tokens", n_segments,
+                    (long long)cu[n_segments], (long long)n_tokens);
+    return H3_OK;
+}
+
+void clear_info(h3_plan_info *info) {
+    if (info) std::memset(info, 0, sizeof *info);
+}
+
+// Shared validation of a relayout contract.
+h3_status check_layout(const h3_layout *L, bool head2seq) {
+    if (!L) return fail(H3_ERR_ARG, "layout is NULL");
+    if (L->reserved != 0) return fail(H3_ERR_ARG, "layout.reserved must be 0");
+    if (L->n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no tokens to partition",
+                                     (long long)L->n_tokens);
+    if (L->n_heads < 1 || L->n_heads > H3_MAX_HEADS)
+        return fail(H3_ERR_ARG, "n_heads = %d; legal values are 1..%d", L->n_heads, H3_MAX_HEADS);
+    if (L->head_dim != H3_HEAD_DIM)
+        return fail(H3_ERR_UNSUPPORTED, "head_dim = %d; only %d is supported", L->head_dim, H3_HEAD_DIM);
+    if (head2seq ? L->n_planes != 1 : (L->n_planes < 1 || L->n_planes > 8))
+        return fail(H3_ERR_ARG, "n_planes = %d; legal values are %s", L->n_planes, head2seq ? "1" : "1..8");
+    const int64_t max_world = std::min<int64_t>(L->n_heads, L->n_tokens);
+    if (L->world < 1 || L->world > max_world)
+        return fail(H3_ERR_EMPTY_PARTITION,
+                    "world = %d would leave a rank without heads or tokens; legal values are 1..%lld",
+                    L->world, (long long)max_world);
+    if (L->world > h3::kMaxRanks)
+        return fail(H3_ERR_UNSUPPORTED, "world = %d; at most %d virtual ranks are supported", L->world,
+                    h3::kMaxRanks);
+    if (L->rank < -1 || L->rank >= L->world)
+        return fail(H3_ERR_ARG, "rank = %d; legal values are -1 (every rank) or 0..%d", L->rank, L->world - 1);
+    if (L->max_chunk_bytes < 0)
+        return fail(H3_ERR_ARG, "max_chunk_bytes = %lld must be >= 0", (long long)L->max_chunk_bytes);
+    const int64_t row_bytes = (int64_t)L->n_heads * L->head_dim * 2;
+    if (L->max_chunk_bytes > 0 && L->max_chunk_bytes < row_bytes)
+        return fail(H3_ERR_ARG, "max_chunk_bytes = %lld is below one token row of one plane (%lld bytes)",
+                    (long long)L->max_chunk_bytes, (long long)row_bytes);
+    return H3_OK;
+}
+
+// Token chunking of one plane: user cap, then the 32-bit index range of the kernel.
+void plan_chunks(const h3_layout *L, uint32_t packed_stride_vec, int64_t *chunk_tokens, int32_t *n_chunks,
+                 int64_t *user_chunk) {
+    const int64_t row_bytes = (int64_t)L->n_heads * L->head_dim * 2;
+    int64_t c = L->max_chunk_bytes > 0 ? L->max_chunk_bytes / row_bytes : L->n_tokens;
+    c = std::min<int64_t>(c, L->n_tokens);
+    *user_chunk = c;
+    // keep t*stride + run and tokens*run below 2^31 inside one launch
+    const int64_t idx_cap = ((int64_t)1 << 31) / ((int64_t)packed_stride_vec + 1) - 1;
+    c = std::max<int64_t>(1, std::min(c, idx_cap));
+    *chunk_tokens = c;
+    *n_chunks = (int32_t)((L->n_tokens + c - 1) / c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *h3_status_string(h3_status st) {
+    switch (st) {
+        case H3_OK: return "H3_OK";
+        case H3_ERR_ARG: return "H3_ERR_ARG";
+        case H3_ERR_EMPTY_PARTITION: return "H3_ERR_EMPTY_PARTITION";
+        case H3_ERR_SEGMENTS: return "H3_ERR_SEGMENTS";
+        case H3_ERR_UNSUPPORTED: return "H3_ERR_UNSUPPORTED";
+        case H3_ERR_ALIAS: return "H3_ERR_ALIAS";
+        case H3_ERR_HIP: return "H3_ERR_HIP";
+    }
+    return "H3_ERR_UNKNOWN";
+}
+
+const char *h3_last_error(void) { return g_last_error; }
+
+const char *h3_version(void) { return "0.1.0"; }
+
+h3_status h3_partition(int64_t total, int32_t parts, int32_t index, int64_t *begin, int64_t *count) {
+    if (!begin || !count) return fail(H3_ERR_ARG, "begin/count is NULL");
+    if (parts < 1 || parts > total)
+        return fail(H3_ERR_EMPTY_PARTITION, "cannot split %lld items over %d ranks without an empty part; "
+                    "legal rank counts are 1..%lld", (long long)total, parts, (long long)total);
+    if (index < 0 || index >= parts)
+        return fail(H3_ERR_ARG, "index = %d; legal values are 0..%d", index, parts - 1);
+    split(total, parts, index, begin, count);
+    return ok();
+}
+
+int32_t h3_clip_segments(const int64_t *cu, int32_t n_segments, int64_t a, int64_t b, int32_t *seg_id,
+                         int64_t *local_begin, int64_t *local_end) {
+    if (!cu || n_segments < 1 || a < 0 || b <= a) {
+        fail(H3_ERR_ARG, "invalid segment table or interval [%lld, %lld)", (long long)a, (long long)b);
+        return -1;
+    }
+    for (int32_t s = 0; s < n_segments; ++s)
+        if (cu[s + 1] <= cu[s] || (s == 0 && cu[0] != 0)) {
+            fail(H3_ERR_SEGMENTS, "segment table is not strictly increasing from 0");
+            return -1;
+        }
+    if (b > cu[n_segments]) {
+        fail(H3_ERR_SEGMENTS, "interval end %lld lies past the last segment (%lld)", (long long)b,
+             (long long)cu[n_segments]);
+        return -1;
+    }
+    int32_t n = 0;
+    for (int32_t s = 0; s < n_segments; ++s) {
+        const int64_t lo = std::max(cu[s], a), hi = std::min(cu[s + 1], b);
+        if (lo < hi) {
+            if (seg_id) seg_id[n] = s;
+            if (local_begin) local_begin[n] = lo - a;
+            if (local_end) local_end[n] = hi - a;
+            ++n;
+        }
+    }
+    ok();
+    return n;
+}
+
+h3_status h3_seq2head(const h3_layout *L, const void *src, void *const *dst, void *stream, h3_plan_info *info) {
+    clear_info(info);
+    h3_status st = check_layout(L, false);
+    if (st != H3_OK) return st;
+    if (!src) return fail(H3_ERR_ARG, "src is NULL");
+    if (!dst) return fail(H3_ERR_ARG, "dst is NULL");
+    const int P = L->world, K = L->n_planes;
+    const int r0 = L->rank < 0 ? 0 : L->rank;
+    const int nr = L->rank < 0 ? P : 1;
+    const uint64_t row_bytes = (uint64_t)L->n_heads * L->head_dim * 2;
+    const uint64_t src_bytes = (uint64_t)L->n_tokens * K * row_bytes;
+
+    std::vector<Range> ins{range_of(src, src_bytes, "src", 0)}, outs;
+    int64_t hb[h3::kMaxRanks], hn[h3::kMaxRanks];
+    for (int j = 0; j < P; ++j) split(L->n_heads, P, j, &hb[j], &hn[j]);
+    for (int j = r0; j < r0 + nr; ++j)
+        for (int p = 0; p < K; ++p) {
+            if (!dst[j * K + p]) return fail(H3_ERR_ARG, "dst[%d] (rank %d, plane %d) is NULL", j * K + p, j, p);
+            outs.push_back(range_of(dst[j * K + p], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "dst",
+                                    j * K + p));
+        }
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+
+    const uint32_t vec_per_head = L->head_dim / 8;
+    const uint32_t stride_vec = (uint32_t)K * L->n_heads * vec_per_head;
+    int64_t chunk, user_chunk;
+    int32_t n_chunks;
+    plan_chunks(L, stride_vec, &chunk, &n_chunks, &user_chunk);
+
+    h3::RunCopyArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint32_t max_run = 0;
+    uint64_t rank_bytes = 0;
+    for (int y = 0; y < nr; ++y) {
+        const int j = r0 + y;
+        a.run_vec[y] = (uint32_t)hn[j] * vec_per_head;
+        a.off_vec[y] = (uint32_t)hb[j] * vec_per_head;
+        a.div[y] = h3::make_fastdiv(a.run_vec[y]);
+        max_run = std::max(max_run, a.run_vec[y]);
+        rank_bytes += (uint64_t)hn[j] * L->head_dim * 2;
+    }
+    a.stride_vec = stride_vec;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int launches = 0, grid_max = 0;
+    for (int p = 0; p < K; ++p) {
+        for (int c = 0; c < n_chunks; ++c) {
+            const int64_t t0 = (int64_t)c * chunk;
+            const int64_t nt = std::min<int64_t>(chunk, L->n_tokens - t0);
+            a.src_packed = static_cast<const char *>(src) + ((uint64_t)t0 * K + p) * row_bytes;
+            for (int y = 0; y < nr; ++y) {
+                const int j = r0 + y;
+                a.dst_rank[y] = static_cast<char *>(dst[j * K + p]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
+            }
+            a.n_tokens = (uint32_t)nt;
+            int gx = 0;
+            hipError_t e = h3::launch_seq2head(a, nr, max_run, s, &gx);
+            if (e != hipSuccess)
+                return fail(H3_ERR_HIP, "seq2head launch (plane %d, chunk %d) failed: %s", p, c, hipGetErrorString(e));
+            ++launches;
+            grid_max = std::max(grid_max, gx);
+        }
+    }
+    if (info) {
+        info->launches = launches;
+        info->chunks = n_chunks;
+        info->grid_x = grid_max;
+        info->block_x = h3::kCopyThreads;
+        info->chunk_tokens = chunk;
+        info->max_launch_src_bytes = (int64_t)(std::min<int64_t>(chunk, L->n_tokens) * rank_bytes);
+        info->bytes_read = (int64_t)((uint64_t)L->n_tokens * K * rank_bytes);
+        info->bytes_written = info->bytes_read;
+    }
+    return ok();
+}
+
+h3_status h3_head2seq(const h3_layout *L, const void *const *src, void *dst, void *stream, h3_plan_info *info) {
+    clear_info(info);
+    h3_status st = check_layout(L, true);
+    if (st != H3_OK) return st;
+    if (!src) return fail(H3_ERR_ARG, "src is NULL");
+    if (!dst) return fail(H3_ERR_ARG, "dst is NULL");
+    const int P = L->world;
+    const int r0 = L->rank < 0 ? 0 : L->rank;
+    const int nr = L->rank < 0 ? P : 1;
+    const uint64_t row_bytes = (uint64_t)L->n_heads * L->head_dim * 2;
+
+    int64_t hb[h3::kMaxRanks], hn[h3::kMaxRanks];
+    for (int j = 0; j < P; ++j) split(L->n_heads, P, j, &hb[j], &hn[j]);
+    std::vector<Range> ins, outs{range_of(dst, (uint64_t)L->n_tokens * row_bytes, "dst", 0)};
+    for (int j = r0; j < r0 + nr; ++j) {
+        if (!src[j]) return fail(H3_ERR_ARG, "src[%d] is NULL", j);
+        ins.push_back(range_of(src[j], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "src", j));
+    }
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+
+    const uint32_t vec_per_head = L->head_dim / 8;
+    const uint32_t stride_vec = (uint32_t)L->n_heads * vec_per_head;
+    int64_t chunk, user_chunk;
+    int32_t n_chunks;
+    plan_chunks(L, stride_vec, &chunk, &n_chunks, &user_chunk);
+
+    h3::RunCopyArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint32_t max_run = 0;
+    uint64_t rank_bytes = 0;
+    for (int y = 0; y < nr; ++y) {
+        const int j = r0 + y;
+        a.run_vec[y] = (uint32_t)hn[j] * vec_per_head;
+        a.off_vec[y] = (uint32_t)hb[j] * vec_per_head;
+        a.div[y] = h3::make_fastdiv(a.run_vec[y]);
+        max_run = std::max(max_run, a.run_vec[y]);
+        rank_bytes += (uint64_t)hn[j] * L->head_dim * 2;
+    }
+    a.stride_vec = stride_vec;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int launches = 0, grid_max = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t t0 = (int64_t)c * chunk;
+        const int64_t nt = std::min<int64_t>(chunk, L->n_tokens - t0);
+        a.dst_packed = static_cast<char *>(dst) + (uint64_t)t0 * row_bytes;
+        for (int y = 0; y < nr; ++y) {
+            const int j = r0 + y;
+            a.src_rank[y] = static_cast<const char *>(src[j]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
+        }
+        a.n_tokens = (uint32_t)nt;
+        int gx = 0;
+        hipError_t e = h3::launch_head2seq(a, nr, max_run, s, &gx);
+        if (e != hipSuccess) return fail(H3_ERR_HIP, "head2seq launch (chunk %d) failed: %s", c, hipGetErrorString(e));
+        ++launches;
+        grid_max = std::max(grid_max, gx);
+    }
+    if (info) {
+        info->launches = launches;
+        info->chunks = n_chunks;
+        info->grid_x = grid_max;
+        info->block_x = h3::kCopyThreads;
+        info->chunk_tokens = chunk;
+        info->max_launch_src_bytes = (int64_t)(std::min<int64_t>(chunk, L->n_tokens) * rank_bytes);
+        info->bytes_read = (int64_t)((uint64_t)L->n_tokens * rank_bytes);
+        info->bytes_written = info->bytes_read;
+    }
+    return ok();
+}
+
+h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void *g, void *o, int64_t n_tokens,
+                         int32_t n_heads, int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale,
+                         void *stream, h3_plan_info *info) {
+    clear_info(info);
+    if (!q || !k || !v || !o) return fail(H3_ERR_ARG, "q, k, v and o must be non-NULL");
+    if (n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no tokens", (long long)n_tokens);
+    if (n_tokens > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens = %lld exceeds 2^31-1", (long long)n_tokens);
+    if (n_heads < 1 || n_heads > H3_MAX_HEADS)
+        return fail(H3_ERR_EMPTY_PARTITION, "n_heads = %d; legal values are 1..%d", n_heads, H3_MAX_HEADS);
+    if (head_dim != H3_HEAD_DIM)
+        return fail(H3_ERR_UNSUPPORTED, "head_dim = %d; only %d is supported", head_dim, H3_HEAD_DIM);
+    if (!(scale > 0.f) || scale != scale || scale > 1e30f)
+        return fail(H3_ERR_ARG, "scale must be a positive finite number");
+    h3_status st = check_segments(cu, n_segments, n_tokens, true);
+    if (st != H3_OK) return st;
+    const uint64_t bytes = (uint64_t)n_tokens * n_heads * head_dim * 2;
+    std::vector<Range> ins{range_of(q, bytes, "q", 0), range_of(k, bytes, "k", 0), range_of(v, bytes, "v", 0)};
+    if (g) ins.push_back(range_of(g, bytes, "g", 0));
+    if ((st = check_alias(ins, {range_of(o, bytes, "o", 0)})) != H3_OK) return st;
+
+    // work list: segments longest first, each expanded to heads x query tiles
+    std::vector<int> order(n_segments);
+    for (int s = 0; s < n_segments; ++s) order[s] = s;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return cu[x + 1] - cu[x] > cu[y + 1] - cu[y]; });
+    h3::AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.o = o;
+    a.n_heads = (uint32_t)n_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.n_entries = n_segments;
+    int64_t total = 0;
+    double flops = 0.0;
+    for (int e = 0; e < n_segments; ++e) {
+        const int s = order[e];
+        const int64_t len = cu[s + 1] - cu[s];
+        a.wg_prefix[e] = (int32_t)total;
+        a.seg_begin[e] = (int32_t)cu[s];
+        a.seg_len[e] = (int32_t)len;
+        total += ((len + h3::kAttnBlockM - 1) / h3::kAttnBlockM) * n_heads;
+        flops += 4.0 * head_dim * n_heads * (double)len * (double)len;
+    }
+    a.wg_prefix[n_segments] = (int32_t)total;
+    if (total > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "too many work tiles");
+    (void)hipGetLastError();
+    hipError_t e = h3::launch_packed_attn(a, (int)total, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "packed attention launch failed: %s", hipGetErrorString(e));
+    if (info) {
+        info->launches = 1;
+        info->chunks = 1;
+        info->grid_x = (int32_t)total;
+        info->block_x = h3::kAttnThreads;
+        info->bytes_read = (int64_t)(bytes * (g ? 4 : 3));
+        info->bytes_written = (int64_t)bytes;
+        info->max_launch_src_bytes = info->bytes_read;
+        info->flops = flops;
+        info->tiles = total;
+    }
+    return ok();
+}
+
+h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,
+                           const void *gate, void *y, int64_t tok_begin, int64_t tok_end, int32_t channels,
+                           const int64_t *cu, int32_t n_segments, float eps, void *stream, h3_plan_info *info) {
+    clear_info(info);
+    if (mode != H3_ADALN_MODULATE && mode != H3_ADALN_GATE_RESIDUAL)
+        return fail(H3_ERR_ARG, "mode = %d; legal values are %d (modulate) and %d (gate residual)", mode,
+                    H3_ADALN_MODULATE, H3_ADALN_GATE_RESIDUAL);
+    if (!x || !y) return fail(H3_ERR_ARG, "x and y must be non-NULL");
+    if (mode == H3_ADALN_MODULATE && (!shift || !scale))
+        return fail(H3_ERR_ARG, "modulate needs shift and scale");
+    if (mode == H3_ADALN_GATE_RESIDUAL && (!branch || !gate))
+        return fail(H3_ERR_ARG, "gate residual needs branch and gate");
+    if (tok_begin < 0 || tok_end <= tok_begin)
+        return fail(H3_ERR_EMPTY_PARTITION, "token interval [%lld, %lld) is empty", (long long)tok_begin,
+                    (long long)tok_end);
+    if (tok_end - tok_begin > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "token interval longer than 2^31-1");
+    if (channels < 8 || channels % 8 != 0 || channels > H3_MAX_CHANNELS)
+        return fail(H3_ERR_UNSUPPORTED, "channels = %d; must be a multiple of 8 in 8..%d", channels,
+                    H3_MAX_CHANNELS);
+    if (mode == H3_ADALN_MODULATE && !(eps >= 0.f && eps < 1e30f))
+        return fail(H3_ERR_ARG, "eps must be a finite number >= 0");
+    h3_status st = check_segments(cu, n_segments, tok_end, false);
+    if (st != H3_OK) return st;
+
+    const int64_t n_rows = tok_end - tok_begin;
+    const uint64_t row_bytes = (uint64_t)channels * 2;
+    const uint64_t par_bytes = (uint64_t)n_segments * row_bytes;
+    std::vector<Range> ins{range_of(x, n_rows * row_bytes, "x", 0)};
+    if (mode == H3_ADALN_MODULATE) {
+        ins.push_back(range_of(shift, par_bytes, "shift", 0));
+        ins.push_back(range_of(scale, par_bytes, "scale", 0));
+    } else {
+        ins.push_back(range_of(branch, n_rows * row_bytes, "branch", 0));
+        ins.push_back(range_of(gate, par_bytes, "gate", 0));
+    }
+    if ((st = check_alias(ins, {range_of(y, n_rows * row_bytes, "y", 0)})) != H3_OK) return st;
+
+    h3::AdalnArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.y = y;
+    a.n_rows = (uint32_t)n_rows;
+    a.channels = (uint32_t)channels;
+    a.eps = eps;
+    a.mode = mode;
+    // clip and rebase the global table to [tok_begin, tok_end)
+    int n = 0;
+    for (int32_t s = 0; s < n_segments; ++s) {
+        const int64_t lo = std::max(cu[s], tok_begin), hi = std::min(cu[s + 1], tok_end);
+        if (lo < hi) {
+            a.entry_begin[n] = (int32_t)(lo - tok_begin);
+            a.entry_seg[n] = s;
+            ++n;
+        }
+    }
+    a.entry_begin[n] = (int32_t)n_rows;
+    a.n_entries = n;
+    (void)hipGetLastError();
+    int gx = 0;
+    hipError_t e = h3::launch_adaln(a, static_cast<hipStream_t>(stream), &gx);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "adaln launch failed: %s", hipGetErrorString(e));
+    if (info) {
+        info->launches = 1;
+        info->chunks = 1;
+        info->grid_x = gx;
+        info->block_x = h3::kAdalnThreads;
+        const uint64_t streams_in = mode == H3_ADALN_MODULATE ? 1 : 2;
+        info->bytes_read = (int64_t)(streams_in * n_rows * row_bytes + (mode == H3_ADALN_MODULATE ? 2 : 1) *
+                                     (uint64_t)n * row_bytes);
+        info->bytes_written = (int64_t)(n_rows * row_bytes);
+        info->max_launch_src_bytes = info->bytes_read;
+        info->tiles = n;
+    }
+    return ok();
+}
+
+}  // extern "C"

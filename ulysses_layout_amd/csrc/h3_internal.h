@@ -1,0 +1,103 @@
+// h3_internal.h -- launch descriptors shared between the host contract
+// (h3_api.hip) and the kernel translation units.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3.h"
+
+namespace h3 {
+
+constexpr int kMaxRanks = 64;           // P <= min(H, N) and H <= 256, but buffers past 64 are not useful
+constexpr int kMaxSegments = H3_MAX_SEGMENTS;
+
+// Unsigned division of n < 2^31 by a runtime-uniform d >= 2 with one
+// multiply-high and one correction step (m = ceil(2^32 / d) overestimates
+// 1/d by less than 2^-32, so the high word is the quotient or one more).
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.m = (uint32_t)(((1ull << 32) + d - 1) / d);
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Relayout: copy of contiguous runs between a "packed" side, where rank j's
+// run of token t starts at t*stride + off_j (in 16-byte vectors), and a
+// "rank" side, where rank j's buffer is dense [tokens][run_j].
+// ---------------------------------------------------------------------------
+struct RunCopyArgs {
+    const void *src_packed;          // seq2head: packed source (plane and chunk offset applied)
+    void *dst_packed;                // head2seq: packed destination (chunk offset applied)
+    const void *src_rank[kMaxRanks]; // head2seq: per selected rank (chunk offset applied)
+    void *dst_rank[kMaxRanks];       // seq2head: per selected rank (chunk offset applied)
+    uint32_t run_vec[kMaxRanks];     // H_j * D / 8 vectors per token
+    uint32_t off_vec[kMaxRanks];     // hb_j * D / 8
+    FastDiv div[kMaxRanks];          // division by run_vec[j]
+    uint32_t stride_vec;             // packed-side token stride in vectors (K*H*D/8 or H*D/8)
+    uint32_t n_tokens;               // tokens in this launch
+    int32_t rank0;                   // rank of grid row y = 0
+};
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 8;       // 16-byte vectors in flight per thread
+
+hipError_t launch_seq2head(const RunCopyArgs &a, int n_ranks, uint32_t max_run, hipStream_t s,
+                           int *grid_x);
+hipError_t launch_head2seq(const RunCopyArgs &a, int n_ranks, uint32_t max_run, hipStream_t s,
+                           int *grid_x);
+
+// ---------------------------------------------------------------------------
+// AdaLN on one token interval, with the clipped and rebased segment table.
+// ---------------------------------------------------------------------------
+struct AdalnArgs {
+    const void *x;
+    const void *branch;
+    const void *shift;
+    const void *scale;
+    const void *gate;
+    void *y;
+    uint32_t n_rows;
+    uint32_t channels;
+    float eps;
+    int32_t mode;
+    int32_t n_entries;
+    int32_t entry_begin[kMaxSegments + 1];   // local first row of entry e; [n_entries] = n_rows
+    int32_t entry_seg[kMaxSegments];         // global segment id of entry e
+};
+
+constexpr int kAdalnThreads = 256;           // 4 waves, one row per wave
+
+hipError_t launch_adaln(const AdalnArgs &a, hipStream_t s, int *grid_x);
+
+// ---------------------------------------------------------------------------
+// Segment-masked attention.  The work list is sorted longest segment first;
+// workgroup w belongs to the sorted segment e with wg_prefix[e] <= w <
+// wg_prefix[e+1], and within it to (head, query tile) with the tile fastest.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *g;          // may be null
+    void *o;
+    uint32_t n_heads;       // heads in the buffers (row stride = n_heads * 128)
+    float scale_log2;       // scale * log2(e)
+    int32_t n_entries;
+    int32_t wg_prefix[kMaxSegments + 1];
+    int32_t seg_begin[kMaxSegments];
+    int32_t seg_len[kMaxSegments];     // query tiles of entry e: ceil(seg_len / kAttnBlockM)
+};
+
+constexpr int kAttnBlockM = 128;       // query rows per workgroup
+constexpr int kAttnThreads = 256;
+
+hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s);
+
+}  // namespace h3

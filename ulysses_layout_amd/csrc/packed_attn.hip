@@ -1,0 +1,249 @@
+// packed_attn.hip -- segment-masked attention over the natively packed
+// multi-segment sequence, for the heads one virtual rank holds after the
+// sequence-to-head relayout ("Distributed H3 Execution", introduction: the
+// packed H3 sequence is kept as is, no semantic padding), with the optional
+// sigmoid gate of the QKVG form ("[perf] Harden Ulysses agreement and tune
+// bounded H3 transfers", Problem and behavior: packed QKV/QKVG operands).
+//
+// Work decomposition: one workgroup = (segment, head, 128-query tile); it
+// walks only the 64-key tiles of its own segment, so cross-segment blocks
+// are never visited and only the last key tile of a segment needs a mask.
+// Segments are issued longest first.  Within a head the query tiles are
+// consecutive workgroup ids, so the workgroups in flight stream the same K/V
+// tiles and share them in L2 and the Infinity Cache.
+//
+// Per wave (64 lanes, 32 query rows), per 64-key tile, with CDNA4's
+// v_mfma_f32_32x32x16_bf16 (A: 32 rows x 16 k, B: 16 k x 32 cols, lane l%32
+// owns row/col l%32, lane half l/32 owns k slots 8*(l/32)..+7; C: lane l%32
+// owns column l%32, register r holds row 8*(r/4) + 4*(l/32) + r%4):
+//   S^T = K Q^T      A = K rows from LDS, B = this wave's Q (registers),
+//                    so each lane ends up holding ONE query and 32 of the
+//                    tile's keys: the softmax row reductions are lane-local
+//                    plus one exchange with lane l^32;
+//   online softmax   base-2 with the log2(e) folded into the scale;
+//   O^T += V^T P^T   B = P^T straight from the S^T registers (the k slots
+//                    of the MFMA are assigned to keys in exactly the order
+//                    the C layout left them in), A = V^T read from a
+//                    transposed copy of the V tile in LDS.
+// The O^T accumulator keeps each lane on its own query, so the rescale by
+// exp2(m_old - m_new) is a per-lane scalar.
+#include "h3_internal.h"
+
+namespace h3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = H3_HEAD_DIM;    // 128
+constexpr int kBN = 64;            // keys per tile
+constexpr int kVtStride = kBN + 4; // padded row of the transposed V tile (elements)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kD];          // swizzled rows
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVtStride];   // V transposed
+
+    // ---- which (segment, head, query tile) this workgroup owns ----------------
+    const int w = blockIdx.x;
+    int lo = 0, hi = a.n_entries - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.wg_prefix[mid] <= w) lo = mid; else hi = mid - 1;
+    }
+    const int seg_len = a.seg_len[lo];
+    const int tiles = (seg_len + kAttnBlockM - 1) / kAttnBlockM;
+    const int local = w - a.wg_prefix[lo];
+    const int head = local / tiles;
+    const int qtile = local - head * tiles;
+    const uint64_t row_stride = (uint64_t)a.n_heads * kD;                    // elements per token
+    const uint64_t base = (uint64_t)a.seg_begin[lo] * row_stride + (uint64_t)head * kD;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    const int q_local = qtile * kAttnBlockM + wave * 32 + l32;            // query of this lane
+    const bool q_valid = q_local < seg_len;
+
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base;
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
+
+    // ---- this lane's query row as the B operand of S^T = K Q^T ----------------
+    bf16x8 qreg[kD / 16];
+    {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qp + (uint64_t)q_local * row_stride);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            u32x4 v = q_valid ? src[ks * 2 + half] : (u32x4){0u, 0u, 0u, 0u};
+            qreg[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // ---- global -> register staging of one K/V tile -----------------------------
+    // thread tid moves rows tid/16 + 16*i (i = 0..3), 16-byte chunk tid%16, of both K and V
+    const int st_row = tid >> 4;
+    const int st_chunk = tid & 15;
+    u32x4 kst[4], vst[4];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = kt * kBN + st_row + 16 * i;
+            if (key < seg_len) {
+                const uint64_t off = (uint64_t)key * row_stride + st_chunk * 8;
+                kst[i] = *reinterpret_cast<const u32x4 *>(kp + off);
+                vst[i] = *reinterpret_cast<const u32x4 *>(vp + off);
+            } else {
+                kst[i] = (u32x4){0u, 0u, 0u, 0u};
+                vst[i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = st_row + 16 * i;
+            *reinterpret_cast<u32x4 *>(&sK[r * kD + ((st_chunk ^ (r & 15)) * 8)]) = kst[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sVt[(st_chunk * 8 + 2 * e) * kVtStride + r] = (uint16_t)(vst[i][e] & 0xffffu);
+                sVt[(st_chunk * 8 + 2 * e + 1) * kVtStride + r] = (uint16_t)(vst[i][e] >> 16);
+            }
+        }
+    };
+
+    f32x16 acc[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
+    float m_run = -__builtin_inff();    // running max, already in log2 units
+    float l_run = 0.f;                  // this lane's share of the running denominator
+
+    const int n_kt = (seg_len + kBN - 1) / kBN;
+    load_tile(0);
+    store_tile();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        __syncthreads();
+        if (kt + 1 < n_kt) load_tile(kt + 1);
+
+        // S^T = K Q^T for the two 32-key blocks of the tile
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = (f32x16){};
+            const int r = kb * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                const int chunk = ks * 2 + half;
+                const u32x4 kv = *reinterpret_cast<const u32x4 *>(&sK[r * kD + ((chunk ^ (r & 15)) * 8)]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks],
+                                                                s[kb], 0, 0, 0);
+            }
+        }
+        // keys past the end of the segment (last tile only)
+        if ((kt + 1) * kBN > seg_len) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * kBN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= seg_len) s[kb][r] = -__builtin_inff();
+                }
+        }
+        // online softmax (base 2)
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = __builtin_fmaxf(m_run, mx * a.scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float psum = 0.f;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kb = j >> 1, r0 = (j & 1) * 8;
+            uint32_t wds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e], a.scale_log2, -m_new));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e + 1], a.scale_log2, -m_new));
+                psum += p0 + p1;
+                wds[e] = pack_bf16x2(p0, p1);
+            }
+            pb[j] = __builtin_bit_cast(bf16x8, (u32x4){wds[0], wds[1], wds[2], wds[3]});
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
+
+        // O^T += V^T P^T; MFMA k slot (half, jj) of step j is key 16j + 8*(jj/4) + 4*half + jj%4
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) {
+            const uint16_t *vrow = &sVt[(db * 32 + l32) * kVtStride + 4 * half];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j);
+                const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j + 8);
+                const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[j],
+                                                                  acc[db], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (kt + 1 < n_kt) store_tile();
+    }
+
+    // ---- epilogue: normalise, gate, round, store ------------------------------
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (!q_valid) return;
+    uint16_t *op = static_cast<uint16_t *>(a.o) + base + (uint64_t)q_local * row_stride;
+    const uint16_t *gp = a.g ? static_cast<const uint16_t *>(a.g) + base + (uint64_t)q_local * row_stride
+                             : nullptr;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            const int d0 = db * 32 + 8 * grp + 4 * half;      // 4 consecutive channels
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = acc[db][grp * 4 + e] * inv;
+            if (gp) {
+                const u32x2 gw = *reinterpret_cast<const u32x2 *>(gp + d0);
+                const float gv[4] = {bf16_lo(gw[0]), bf16_hi(gw[0]), bf16_lo(gw[1]), bf16_hi(gw[1])};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // sigmoid(g) = 1 / (1 + 2^(-g * log2 e))
+                    const float den = 1.0f + __builtin_amdgcn_exp2f(-gv[e] * 1.4426950408889634f);
+                    y[e] = y[e] / den;
+                }
+            }
+            const u32x2 out = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            *reinterpret_cast<u32x2 *>(op + d0) = out;
+        }
+    }
+}
+
+hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s) {
+    if (n_workgroups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_packed_attn, dim3(n_workgroups), dim3(kAttnThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace h3
