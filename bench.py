@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the Ulysses H3 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input
+already resident in HBM: seq2head of the packed QKVG operand (plane at a time),
+segment-masked gated attention for the rank's heads, head2seq, and per-segment
+AdaLN modulation over every virtual rank's token interval.  The default
+workload is 131072 packed tokens (segments 98304 + 32768), P = 4 virtual
+ranks, one rank's share of 14 heads.
+
+Prints ONE JSON line.  ``value`` is the packed-attention throughput in TFLOP/s
+(algorithmic FLOPs of the step's attention / time of its attention launch);
+relayout and AdaLN rates are reported under ``components``.  ``roofline``
+describes the dominant kernel (the attention) against MI355X's dense bf16
+MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "packed-attn TFLOP/s + relayout GB/s (% of roofline) at 32k/128k/250k tokens"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+ATTN_KERNEL = "k_packed_attn"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "packed_attn_128k_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="128k_p4_qkvg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle sample (attention part)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    path = os.path.join(ROOT, "ulysses_layout_amd", "csrc", "packed_attn.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(flops_per_launch: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(step, workload, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.default_threads()
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    src = bits(step.qkv)
+    j = step.attn_ranks[0]
+    t0 = time.perf_counter()
+    bufs = oracle.seq2head(src, step.world, ranks=[j])
+    relayout_s = time.perf_counter() - t0
+    relayout_bytes = 2 * sum(b.nbytes for b in bufs.values())
+    q, k, v = bufs[(j, 0)], bufs[(j, 1)], bufs[(j, 2)]
+    g = bufs[(j, 3)] if step.gated else None
+    del src
+    # attention rows: seeded random rows, batches of 16, until the budget is spent
+    rng = np.random.default_rng(workload.seed)
+    cu = step.cu
+    seg_len = np.diff(np.asarray(cu))
+    done_rows, flops, spent = 0, 0.0, 0.0
+    heads = q.shape[1]
+    while spent < budget_s:
+        rows = np.sort(rng.integers(0, step.n_tokens, size=16))
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, g, cu, step.scale, rows=rows, threads=threads)
+        spent += time.perf_counter() - t0
+        seg_of = np.searchsorted(np.asarray(cu), rows, side="right") - 1
+        flops += float(4 * 128 * heads * seg_len[seg_of].sum())
+        done_rows += len(rows)
+    # AdaLN modulation on the first 4096 rows of rank 0's interval
+    xb = bits(step.x[:4096])
+    prm = [bits(t) for t in (step.shift, step.ada_scale)]
+    t0 = time.perf_counter()
+    oracle.adaln_rows(0, xb, None, prm[0], prm[1], None, 0, 4096, cu, step.eps, threads=threads)
+    adaln_s = time.perf_counter() - t0
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 attention of {done_rows} seeded random query rows x {heads} heads over their full "
+                   f"segments ({flops:.3e} FLOP in {spent:.1f} s); relayout: oracle seq2head of rank {j}'s "
+                   f"share, all {step.planes} planes; AdaLN: 4096 modulated rows"),
+        "relayout_GBps": relayout_bytes / relayout_s / 1e9,
+        "adaln_GBps": 2 * xb.nbytes / adaln_s / 1e9,
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build emulates the P sequence-parallel ranks as "
+              f"virtual-rank buffers on a single device and issues no collectives; --gpus {args.gpus} "
+              f"is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import WORKLOADS
+    from synth.inputs import normal_bf16
+    from ulysses_layout_amd.pipeline import UlyssesStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    attn_ranks = None if w.attn_rank is None else [w.attn_rank]
+    step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
+                       max_chunk_bytes=w.max_chunk_bytes)
+    step.qkv.copy_(normal_bf16(step.qkv.shape, seed=w.seed, device="cuda"))
+    step.x.copy_(normal_bf16(step.x.shape, seed=w.seed + 1, device="cuda"))
+    for i, t in enumerate((step.shift, step.ada_scale, step.gate)):
+        t.copy_(normal_bf16(t.shape, seed=w.seed + 3 + i, std=0.1, device="cuda"))
+    torch.cuda.synchronize()
+
+    names = ("seq2head", "attention", "head2seq", "adaln")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    events = [{n: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for n in names}
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(events=events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in events) / args.steps for n in names}
+
+    attn_flops = step.attention_flops()
+    rb = step.relayout_bytes()
+    attn_launches = len(step.attn_ranks)
+    attn_tflops = attn_flops / (ms["attention"] * 1e-3) / 1e12
+    s2h_gbps = rb["seq2head"] / (ms["seq2head"] * 1e-3) / 1e9
+    h2s_gbps = rb["head2seq"] / (ms["head2seq"] * 1e-3) / 1e9
+    ada_gbps = step.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9
+    flops_per_launch = attn_flops / attn_launches
+    launch_ms = ms["attention"] / attn_launches
+    traffic = read_traffic(flops_per_launch)
+
+    components = {
+        "seq2head": {"ms": ms["seq2head"], "GBps": s2h_gbps, "frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
+                     "bytes": rb["seq2head"], "launches": sum(p.launches for p in step.last_plans["seq2head"])},
+        "attention": {"ms": ms["attention"], "TFLOPs": attn_tflops, "frac_bf16": attn_tflops / PEAK_BF16_TFLOPS,
+                      "flops": attn_flops, "launches": attn_launches},
+        "head2seq": {"ms": ms["head2seq"], "GBps": h2s_gbps, "frac_hbm": h2s_gbps / PEAK_HBM_GBPS,
+                     "bytes": rb["head2seq"]},
+        "adaln": {"ms": ms["adaln"], "GBps": ada_gbps, "frac_hbm": ada_gbps / PEAK_HBM_GBPS,
+                  "bytes": step.adaln_bytes(), "launches": len(step.last_plans["adaln"])},
+    }
+    result = {
+        "metric": METRIC,
+        "value": attn_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 operands, real packed-segment layout)",
+        "config": {
+            "workload": w.name,
+            "n_tokens": w.n_tokens,
+            "segments": w.segment_lengths,
+            "virtual_ranks": w.world,
+            "heads_per_rank": [c for _, c in step.heads],
+            "attention_ranks": step.attn_ranks,
+            "planes": w.planes,
+            "head_dim": 128,
+            "relayout": "every rank" if w.relayout_rank < 0 else f"rank {w.relayout_rank} share",
+            "max_chunk_bytes": w.max_chunk_bytes,
+            "adaln_rows": w.n_tokens,
+            "channels": step.channels,
+        },
+        "relayout_GBps": (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3) / 1e9,
+        "relayout_frac_hbm": (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3)
+        / 1e9 / PEAK_HBM_GBPS,
+        "components": components,
+        "roofline": {
+            "kernel": ATTN_KERNEL,
+            "bound": "mfma",
+            "achieved": flops_per_launch / (launch_ms * 1e-3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_per_launch / (launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "avg_launch_ms": launch_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(step, w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

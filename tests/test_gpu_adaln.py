@@ -90,7 +90,7 @@ def test_adaln_workload(name):
     xb, bb = to_bits(x), to_bits(b)
     pb = [to_bits(t) for t in prm]
     for a, cnt in parts:
-        rows = sample_rows([0] + [e - a for _, _, e in oracle.clip_segments(w.cu, a, a + cnt)],
+        rows = sample_rows([0] + [e for _, _, e in oracle.clip_segments(w.cu, a, a + cnt)],
                            seed=w.seed + a, per_tile=512, limit=600)
         for mode, out in ((0, y), (1, yg)):
             ref = oracle.adaln_rows(mode, xb[a:a + cnt], bb[a:a + cnt], pb[0], pb[1], pb[2], a, a + cnt, w.cu,
