@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample (attention part)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="first run a plain torch copy of this many MiB three times, so hardware byte "
+                         "counters can be scaled against a transfer of known size")
     return ap.parse_args()
 
 
@@ -139,6 +142,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {n} bytes read and {n} bytes written per launch, 3 launches", file=sys.stderr)
+        del a, b
     w = WORKLOADS[args.workload]
     attn_ranks = None if w.attn_rank is None else [w.attn_rank]
     step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
