@@ -16,31 +16,47 @@
 // v_mfma_f32_32x32x16_bf16 (A: 32 rows x 16 k, B: 16 k x 32 cols, lane l%32
 // owns row/col l%32, lane half l/32 owns k slots 8*(l/32)..+7; C: lane l%32
 // owns column l%32, register r holds row 8*(r/4) + 4*(l/32) + r%4):
-//   S^T = K Q^T      A = K rows from LDS, B = this wave's Q (registers),
-//                    so each lane ends up holding ONE query and 32 of the
-//                    tile's keys: the softmax row reductions are lane-local
-//                    plus one exchange with lane l^32;
-//   online softmax   base-2 with the log2(e) folded into the scale;
-//   O^T += V^T P^T   B = P^T straight from the S^T registers (the k slots
-//                    of the MFMA are assigned to keys in exactly the order
-//                    the C layout left them in), A = V^T read from a
-//                    transposed copy of the V tile in LDS.
-// The O^T accumulator keeps each lane on its own query, so the rescale by
-// exp2(m_old - m_new) is a per-lane scalar.
+//   S^T = K Q^T      A = K rows from LDS, B = this wave's Q (registers), so
+//                    each lane holds ONE query and 32 of the tile's keys: the
+//                    softmax row reductions are lane-local plus one exchange
+//                    with lane l^32;
+//   online softmax   base 2, log2(e) folded into the scale; the running max
+//                    is only raised when a row's new maximum exceeds it by
+//                    more than 2^8 (probabilities stay <= 256, exact in the
+//                    final normalisation), so the O rescale is rare;
+//   O^T += V^T P^T   B = P^T straight from the S^T registers (the MFMA k
+//                    slots are assigned to keys in exactly the order the C
+//                    layout left them in), A = V^T read with the gfx950
+//                    transposing LDS load ds_read_b64_tr_b16 from the
+//                    row-major V tile (per 16-lane group it turns a 4-key x
+//                    16-channel block into one channel x 4 keys per lane).
+// The O^T accumulator keeps each lane on its own query, so the rescale is a
+// per-lane scalar and the row sum of P comes from v_dot2 on the rounded bf16
+// P the MFMA consumes.
+//
+// LDS: K and V tiles [64][128] bf16, double buffered (one barrier per tile).
+// 16-byte chunk c of row r sits at chunk c ^ f(r), f(r) = 4*(r%4) + (r/4)%4:
+// 16 consecutive rows read at one logical chunk, and the 4 rows x 4 chunks a
+// 32-lane half reads through the transposing load, both hit 16 distinct
+// chunk positions (all 64 banks), and the global->LDS row writes are
+// permutations within a row.
 #include "h3_internal.h"
 
 namespace h3 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kD = H3_HEAD_DIM;    // 128
-constexpr int kBN = 64;            // keys per tile
-constexpr int kVtStride = kBN + 4; // padded row of the transposed V tile (elements)
+constexpr int kD = H3_HEAD_DIM;          // 128
+constexpr int kBN = 64;                  // keys per tile
+constexpr int kTileElems = kBN * kD;     // one K or V tile
+constexpr float kLazyRescale = 8.0f;     // log2 of the largest tolerated probability
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 f = {lo, hi};
@@ -51,9 +67,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// element offset of (row r, 16-byte chunk c) inside a swizzled tile
+__device__ __forceinline__ int swz(int r, int c) {
+    const int f = ((r & 3) << 2) | ((r >> 2) & 3);
+    return r * kD + ((c ^ f) << 3);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(__attribute__((address_space(3))) void *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kD];          // swizzled rows
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * kVtStride];   // V transposed
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kTileElems];
 
     // ---- which (segment, head, query tile) this workgroup owns ----------------
     const int w = blockIdx.x;
@@ -93,6 +123,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
         }
     }
 
+    // ---- per-lane LDS offsets (independent of the tile and of kb / j) ---------
+    int k_off[kD / 16];                        // A operand of S^T: row l32 (+32 kb), chunk 2ks+half
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) k_off[ks] = swz(l32, 2 * ks + half);
+    int v_off[kD / 32][2];                     // transposing reads: keys 16j + 8 s2 + 4 half + i/4
+    {
+        const int grp = lane >> 4, i = lane & 15;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int r = 8 * s2 + 4 * half + (i >> 2);
+                const int col = db * 32 + 16 * (grp & 1) + 4 * (i & 3);
+                v_off[db][s2] = swz(r, col >> 3) + (col & 7);
+            }
+    }
+
     // ---- global -> register staging of one K/V tile -----------------------------
     // thread tid moves rows tid/16 + 16*i (i = 0..3), 16-byte chunk tid%16, of both K and V
     const int st_row = tid >> 4;
@@ -112,16 +159,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = st_row + 16 * i;
-            *reinterpret_cast<u32x4 *>(&sK[r * kD + ((st_chunk ^ (r & 15)) * 8)]) = kst[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sVt[(st_chunk * 8 + 2 * e) * kVtStride + r] = (uint16_t)(vst[i][e] & 0xffffu);
-                sVt[(st_chunk * 8 + 2 * e + 1) * kVtStride + r] = (uint16_t)(vst[i][e] >> 16);
-            }
+            const int off = swz(st_row + 16 * i, st_chunk);
+            *reinterpret_cast<u32x4 *>(&sK[buf][off]) = kst[i];
+            *reinterpret_cast<u32x4 *>(&sV[buf][off]) = vst[i];
         }
     };
 
@@ -130,25 +173,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
     for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
     float m_run = -__builtin_inff();    // running max, already in log2 units
     float l_run = 0.f;                  // this lane's share of the running denominator
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     const int n_kt = (seg_len + kBN - 1) / kBN;
     load_tile(0);
-    store_tile();
+    store_tile(0);
 
     for (int kt = 0; kt < n_kt; ++kt) {
-        __syncthreads();
+        const int buf = kt & 1;
+        __syncthreads();                 // tile kt is in sK/sV[buf]; buf^1 is free
         if (kt + 1 < n_kt) load_tile(kt + 1);
+        const uint16_t *tk = sK[buf];
+        const uint16_t *tv = sV[buf];
 
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = (f32x16){};
-            const int r = kb * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
-                const int chunk = ks * 2 + half;
-                const u32x4 kv = *reinterpret_cast<const u32x4 *>(&sK[r * kD + ((chunk ^ (r & 15)) * 8)]);
+                const u32x4 kv = *reinterpret_cast<const u32x4 *>(tk + kb * 32 * kD + k_off[ks]);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks],
                                                                 s[kb], 0, 0, 0);
             }
@@ -163,15 +208,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
                     if (key >= seg_len) s[kb][r] = -__builtin_inff();
                 }
         }
-        // online softmax (base 2)
+        // online softmax (base 2) with lazy rescaling
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = __builtin_fmaxf(m_run, mx * a.scale_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+            const float m_new = __builtin_fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
         float psum = 0.f;
         bf16x8 pb[4];
 #pragma unroll
@@ -180,33 +231,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
             uint32_t wds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e], a.scale_log2, -m_new));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e + 1], a.scale_log2, -m_new));
-                psum += p0 + p1;
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e], a.scale_log2, -m_run));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e + 1], a.scale_log2, -m_run));
                 wds[e] = pack_bf16x2(p0, p1);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wds[e]), ones, psum, false);
             }
             pb[j] = __builtin_bit_cast(bf16x8, (u32x4){wds[0], wds[1], wds[2], wds[3]});
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
+        l_run += psum;
 
         // O^T += V^T P^T; MFMA k slot (half, jj) of step j is key 16j + 8*(jj/4) + 4*half + jj%4
 #pragma unroll
         for (int db = 0; db < kD / 32; ++db) {
-            const uint16_t *vrow = &sVt[(db * 32 + l32) * kVtStride + 4 * half];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32x2 v0 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j);
-                const u32x2 v1 = *reinterpret_cast<const u32x2 *>(vrow + 16 * j + 8);
-                const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[j],
-                                                                  acc[db], 0, 0, 0);
+                const bf16x4 v0 = lds_read_tr(tv + 16 * j * kD + v_off[db][0]);
+                const bf16x4 v1 = lds_read_tr(tv + 16 * j * kD + v_off[db][1]);
+                const bf16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], acc[db], 0, 0, 0);
             }
         }
-        __syncthreads();
-        if (kt + 1 < n_kt) store_tile();
+        if (kt + 1 < n_kt) store_tile(buf ^ 1);
     }
 
     // ---- epilogue: normalise, gate, round, store ------------------------------
