@@ -95,8 +95,8 @@ struct AttnArgs {
     int32_t seg_len[kMaxSegments];     // query tiles of entry e: ceil(seg_len / kAttnBlockM)
 };
 
-constexpr int kAttnBlockM = 128;       // query rows per workgroup
-constexpr int kAttnThreads = 256;
+constexpr int kAttnBlockM = 256;       // query rows per workgroup (32 per wave)
+constexpr int kAttnThreads = 512;      // 8 waves
 
 hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s);
 

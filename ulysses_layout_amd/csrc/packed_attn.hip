@@ -5,12 +5,13 @@
 // sigmoid gate of the QKVG form ("[perf] Harden Ulysses agreement and tune
 // bounded H3 transfers", Problem and behavior: packed QKV/QKVG operands).
 //
-// Work decomposition: one workgroup = (segment, head, 128-query tile); it
-// walks only the 64-key tiles of its own segment, so cross-segment blocks
-// are never visited and only the last key tile of a segment needs a mask.
-// Segments are issued longest first.  Within a head the query tiles are
-// consecutive workgroup ids, so the workgroups in flight stream the same K/V
-// tiles and share them in L2 and the Infinity Cache.
+// Work decomposition: one workgroup of 8 waves = (segment, head, 256-query
+// tile); it walks only the 64-key tiles of its own segment, so cross-segment
+// blocks are never visited and only the last key tile of a segment needs a
+// mask.  Segments are issued longest first.  Within a head the query tiles
+// are consecutive workgroup ids, so the workgroups in flight stream the same
+// K/V tiles and share them in L2 and the Infinity Cache; 256 queries per
+// workgroup halve the K/V traffic per FLOP against 128.
 //
 // Per wave (64 lanes, 32 query rows), per 64-key tile, with CDNA4's
 // v_mfma_f32_32x32x16_bf16 (A: 32 rows x 16 k, B: 16 k x 32 cols, lane l%32
@@ -34,12 +35,18 @@
 // per-lane scalar and the row sum of P comes from v_dot2 on the rounded bf16
 // P the MFMA consumes.
 //
-// LDS: K and V tiles [64][128] bf16, double buffered (one barrier per tile).
-// 16-byte chunk c of row r sits at chunk c ^ f(r), f(r) = 4*(r%4) + (r/4)%4:
-// 16 consecutive rows read at one logical chunk, and the 4 rows x 4 chunks a
+// K/V tiles move from HBM straight into LDS with the gfx950 128-bit
+// global_load_lds (no VGPR staging): wave w's i-th load fills LDS bytes
+// [1 KB*(8i + w), +1 KB), i.e. rows 4(8i+w)..+3, lane l at 16-byte slot l.
+// LDS holds K and V tiles [64][128] bf16, double buffered (one barrier per
+// tile, the loop unrolled by two so buffer offsets are immediates).  16-byte
+// chunk c of row r sits at chunk c ^ f(r), f(r) = 4*(r%4) + (r/4)%4: 16
+// consecutive rows read at one logical chunk, and the 4 rows x 4 chunks a
 // 32-lane half reads through the transposing load, both hit 16 distinct
-// chunk positions (all 64 banks), and the global->LDS row writes are
-// permutations within a row.
+// chunk positions.  Because the LDS side of a direct load is fixed per lane,
+// the swizzle is applied on the global side: lane l of a load fetches logical
+// chunk (l%16) ^ f(row).  Rows past the end of the segment are clamped to
+// its last row (finite data, masked out or weighted by 0).
 #include "h3_internal.h"
 
 namespace h3 {
@@ -56,7 +63,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kD = H3_HEAD_DIM;          // 128
 constexpr int kBN = 64;                  // keys per tile
 constexpr int kTileElems = kBN * kD;     // one K or V tile
+constexpr int kWaves = kAttnThreads / 64;
+constexpr int kLoadsPerTile = kBN / (4 * kWaves);   // 16-byte direct loads per lane per operand
 constexpr float kLazyRescale = 8.0f;     // log2 of the largest tolerated probability
+static_assert(kAttnBlockM == 32 * kWaves, "one 32-query block per wave");
+static_assert(kLoadsPerTile * 4 * kWaves == kBN, "loads cover the tile");
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 f = {lo, hi};
@@ -67,21 +78,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+__device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // element offset of (row r, 16-byte chunk c) inside a swizzled tile
-__device__ __forceinline__ int swz(int r, int c) {
-    const int f = ((r & 3) << 2) | ((r >> 2) & 3);
-    return r * kD + ((c ^ f) << 3);
-}
+__device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r)) << 3); }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(__attribute__((address_space(3))) void *)(p));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_void *)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][kTileElems];
 
@@ -115,10 +125,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
     // ---- this lane's query row as the B operand of S^T = K Q^T ----------------
     bf16x8 qreg[kD / 16];
     {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(qp + (uint64_t)q_local * row_stride);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qp + (uint64_t)(q_valid ? q_local : 0) * row_stride);
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks) {
-            u32x4 v = q_valid ? src[ks * 2 + half] : (u32x4){0u, 0u, 0u, 0u};
+            u32x4 v = src[ks * 2 + half];
+            if (!q_valid) v = (u32x4){0u, 0u, 0u, 0u};
             qreg[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -140,31 +151,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
             }
     }
 
-    // ---- global -> register staging of one K/V tile -----------------------------
-    // thread tid moves rows tid/16 + 16*i (i = 0..3), 16-byte chunk tid%16, of both K and V
-    const int st_row = tid >> 4;
-    const int st_chunk = tid & 15;
-    u32x4 kst[4], vst[4];
-    auto load_tile = [&](int kt) {
+    // ---- direct HBM -> LDS tile loads ------------------------------------------
+    // load i of wave `wave` covers tile rows 4*(kWaves*i + wave) .. +3, lane l row +l/16;
+    // f(row) does not depend on i because rows step by 4*kWaves (a multiple of 16).
+    const int ld_row0 = 4 * wave + (lane >> 4);
+    const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
+    const int n_kt = (seg_len + kBN - 1) / kBN;
+    auto issue_tile = [&](int kt, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = kt * kBN + st_row + 16 * i;
-            if (key < seg_len) {
-                const uint64_t off = (uint64_t)key * row_stride + st_chunk * 8;
-                kst[i] = *reinterpret_cast<const u32x4 *>(kp + off);
-                vst[i] = *reinterpret_cast<const u32x4 *>(vp + off);
-            } else {
-                kst[i] = (u32x4){0u, 0u, 0u, 0u};
-                vst[i] = (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int off = swz(st_row + 16 * i, st_chunk);
-            *reinterpret_cast<u32x4 *>(&sK[buf][off]) = kst[i];
-            *reinterpret_cast<u32x4 *>(&sV[buf][off]) = vst[i];
+        for (int i = 0; i < kLoadsPerTile; ++i) {
+            int key = kt * kBN + ld_row0 + 4 * kWaves * i;
+            key = key < seg_len ? key : seg_len - 1;
+            const uint64_t off = (uint64_t)key * row_stride + ld_chunk * 8;
+            const int lds_row = 4 * (kWaves * i + wave);            // wave-uniform
+            __builtin_amdgcn_global_load_lds(kp + off, (lds_void *)(&sK[buf][lds_row * kD]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vp + off, (lds_void *)(&sV[buf][lds_row * kD]), 16, 0, 0);
         }
     };
 
@@ -175,17 +176,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
     float l_run = 0.f;                  // this lane's share of the running denominator
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    const int n_kt = (seg_len + kBN - 1) / kBN;
-    load_tile(0);
-    store_tile(0);
-
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
-        __syncthreads();                 // tile kt is in sK/sV[buf]; buf^1 is free
-        if (kt + 1 < n_kt) load_tile(kt + 1);
-        const uint16_t *tk = sK[buf];
-        const uint16_t *tv = sV[buf];
-
+    auto compute_tile = [&](int kt, const uint16_t *tk, const uint16_t *tv) {
         // S^T = K Q^T for the two 32-key blocks of the tile
         f32x16 s[2];
 #pragma unroll
@@ -251,7 +242,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_packed_attn(AttnArgs a) {
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], acc[db], 0, 0, 0);
             }
         }
-        if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    };
+
+    // ---- main loop: two tiles per trip so each buffer index is an immediate ---
+    issue_tile(0, 0);
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): this lane's loads of tile kt landed
+        __syncthreads();                              // ... and everyone's; buffer 1 is free
+        if (kt + 1 < n_kt) issue_tile(kt + 1, 1);
+        compute_tile(kt, sK[0], sV[0]);
+        if (kt + 1 >= n_kt) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (kt + 2 < n_kt) issue_tile(kt + 2, 0);
+        compute_tile(kt + 1, sK[1], sV[1]);
     }
 
     // ---- epilogue: normalise, gate, round, store ------------------------------
