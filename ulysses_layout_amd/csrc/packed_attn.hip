@@ -39,7 +39,7 @@
 // global_load_lds (no VGPR staging): wave w's i-th load fills LDS bytes
 // [1 KB*(8i + w), +1 KB), i.e. rows 4(8i+w)..+3, lane l at 16-byte slot l.
 // LDS holds K and V tiles [64][128] bf16, double buffered (one barrier per
-// tile, the loop unrolled by two so buffer offsets are immediates).  16-byte
+// tile, the loop unrolled by two so buffer addresses are constants).  16-byte
 // chunk c of row r sits at chunk c ^ f(r), f(r) = 4*(r%4) + (r/4)%4: 16
 // consecutive rows read at one logical chunk, and the 4 rows x 4 chunks a
 // 32-lane half reads through the transposing load, both hit 16 distinct
@@ -92,8 +92,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
 }
 
 __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kTileElems];
+    // Four distinct LDS objects (not one array of buffers) so the compiler can
+    // prove that the direct loads into one buffer never alias the reads of the
+    // other and does not serialise them with extra counter waits.
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kTileElems];
 
     // ---- which (segment, head, query tile) this workgroup owns ----------------
     const int w = blockIdx.x;
@@ -157,15 +162,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const int ld_row0 = 4 * wave + (lane >> 4);
     const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
     const int n_kt = (seg_len + kBN - 1) / kBN;
-    auto issue_tile = [&](int kt, int buf) {
+    auto issue_tile = [&](int kt, uint16_t *dk, uint16_t *dv) {
 #pragma unroll
         for (int i = 0; i < kLoadsPerTile; ++i) {
             int key = kt * kBN + ld_row0 + 4 * kWaves * i;
             key = key < seg_len ? key : seg_len - 1;
             const uint64_t off = (uint64_t)key * row_stride + ld_chunk * 8;
             const int lds_row = 4 * (kWaves * i + wave);            // wave-uniform
-            __builtin_amdgcn_global_load_lds(kp + off, (lds_void *)(&sK[buf][lds_row * kD]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vp + off, (lds_void *)(&sV[buf][lds_row * kD]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kp + off, (lds_void *)(dk + lds_row * kD), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vp + off, (lds_void *)(dv + lds_row * kD), 16, 0, 0);
         }
     };
 
@@ -245,17 +250,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     };
 
     // ---- main loop: two tiles per trip so each buffer index is an immediate ---
-    issue_tile(0, 0);
+    issue_tile(0, sK0, sV0);
     for (int kt = 0; kt < n_kt; kt += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): this lane's loads of tile kt landed
         __syncthreads();                              // ... and everyone's; buffer 1 is free
-        if (kt + 1 < n_kt) issue_tile(kt + 1, 1);
-        compute_tile(kt, sK[0], sV[0]);
+        if (kt + 1 < n_kt) issue_tile(kt + 1, sK1, sV1);
+        compute_tile(kt, sK0, sV0);
         if (kt + 1 >= n_kt) break;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (kt + 2 < n_kt) issue_tile(kt + 2, 0);
-        compute_tile(kt + 1, sK[1], sV[1]);
+        if (kt + 2 < n_kt) issue_tile(kt + 2, sK0, sV0);
+        compute_tile(kt + 1, sK1, sV1);
     }
 
     // ---- epilogue: normalise, gate, round, store ------------------------------
