@@ -35,9 +35,15 @@
 // per-lane scalar and the row sum of P comes from v_dot2 on the rounded bf16
 // P the MFMA consumes.
 //
-// K/V tiles move from HBM straight into LDS with the gfx950 128-bit
-// global_load_lds (no VGPR staging): wave w's i-th load fills LDS bytes
+// K/V tiles move from HBM straight into LDS with the 128-bit buffer load to
+// LDS (no VGPR staging): wave w's i-th load fills LDS bytes
 // [1 KB*(8i + w), +1 KB), i.e. rows 4(8i+w)..+3, lane l at 16-byte slot l.
+// The buffer resource is rebased to each tile's first key, so the per-lane
+// offsets stay below 64 rows.  The buffer form rather than the global one is
+// deliberate: the compiler treats an outstanding global load to LDS like a
+// flat access that may also count on the LDS counter, and then drains every
+// LDS read completely before its first use; with the buffer form it keeps
+// exact per-read waits, so K fragments stream into the QK MFMAs.
 // LDS holds K and V tiles [64][128] bf16, double buffered (one barrier per
 // tile, the loop unrolled by two so buffer addresses are constants).  16-byte
 // chunk c of row r sits at chunk c ^ f(r), f(r) = 4*(r%4) + (r/4)%4: 16
@@ -66,6 +72,9 @@ constexpr int kTileElems = kBN * kD;     // one K or V tile
 constexpr int kWaves = kAttnThreads / 64;
 constexpr int kLoadsPerTile = kBN / (4 * kWaves);   // 16-byte direct loads per lane per operand
 constexpr float kLazyRescale = 8.0f;     // log2 of the largest tolerated probability
+constexpr int kBufferWord3 = 0x00020000; // buffer resource word 3 for raw 32-bit data on gfx9-class parts
+constexpr int kSchedMfma = 0x008;        // sched_group_barrier class masks
+constexpr int kSchedDsRead = 0x100;
 static_assert(kAttnBlockM == 32 * kWaves, "one 32-query block per wave");
 static_assert(kLoadsPerTile * 4 * kWaves == kBN, "loads cover the tile");
 
@@ -85,6 +94,16 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// reductions across the two 32-lane halves (lane l and lane l ^ 32)
+__device__ __forceinline__ float half_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_void *)(p));
@@ -162,15 +181,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const int ld_row0 = 4 * wave + (lane >> 4);
     const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
     const int n_kt = (seg_len + kBN - 1) / kBN;
+    const int row_bytes = (int)(row_stride * 2);       // <= 256 heads * 256 B
     auto issue_tile = [&](int kt, uint16_t *dk, uint16_t *dv) {
+        const uint64_t tile0 = (uint64_t)kt * kBN * row_stride;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kp + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vp + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const int last = seg_len - 1 - kt * kBN;          // last key of the segment, tile-relative
 #pragma unroll
         for (int i = 0; i < kLoadsPerTile; ++i) {
-            int key = kt * kBN + ld_row0 + 4 * kWaves * i;
-            key = key < seg_len ? key : seg_len - 1;
-            const uint64_t off = (uint64_t)key * row_stride + ld_chunk * 8;
+            int key = ld_row0 + 4 * kWaves * i;
+            key = key < last ? key : last;
+            const int off = key * row_bytes + ld_chunk * 16;
             const int lds_row = 4 * (kWaves * i + wave);            // wave-uniform
-            __builtin_amdgcn_global_load_lds(kp + off, (lds_void *)(dk + lds_row * kD), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vp + off, (lds_void *)(dv + lds_row * kD), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + lds_row * kD), 16, off, 0, 0, 0);
         }
     };
 
@@ -182,18 +208,37 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     auto compute_tile = [&](int kt, const uint16_t *tk, const uint16_t *tv) {
-        // S^T = K Q^T for the two 32-key blocks of the tile
+        // S^T = K Q^T for the two 32-key blocks of the tile: fragment i is block i%2,
+        // k step i/2, so the two accumulation chains alternate.  The reads run four
+        // ahead of the MFMAs that consume them.
         f32x16 s[2];
+        s[0] = (f32x16){};
+        s[1] = (f32x16){};
+        bf16x8 kf[16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = (f32x16){};
+        for (int i = 0; i < 16; ++i)
+            kf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(tk + (i & 1) * 32 * kD + k_off[i >> 1]));
 #pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks) {
-                const u32x4 kv = *reinterpret_cast<const u32x4 *>(tk + kb * 32 * kD + k_off[ks]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks],
-                                                                s[kb], 0, 0, 0);
-            }
+        for (int i = 0; i < 16; ++i)
+            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[i >> 1], s[i & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        // V^T fragments for the PV step, read now so they land during the softmax;
+        // fragment (db, j) covers channels 32db.. and keys 16j..16j+15
+        bf16x8 vf[kD / 32][4];
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x4 v0 = lds_read_tr(tv + 16 * j * kD + v_off[db][0]);
+                const bf16x4 v1 = lds_read_tr(tv + 16 * j * kD + v_off[db][1]);
+                vf[db][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         // keys past the end of the segment (last tile only)
         if ((kt + 1) * kBN > seg_len) {
 #pragma unroll
@@ -210,7 +255,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+        mx = half_max(mx) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
             const float m_new = __builtin_fmaxf(m_run, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -238,15 +283,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
 
         // O^T += V^T P^T; MFMA k slot (half, jj) of step j is key 16j + 8*(jj/4) + 4*half + jj%4
 #pragma unroll
-        for (int db = 0; db < kD / 32; ++db) {
+        for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x4 v0 = lds_read_tr(tv + 16 * j * kD + v_off[db][0]);
-                const bf16x4 v1 = lds_read_tr(tv + 16 * j * kD + v_off[db][1]);
-                const bf16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[j], acc[db], 0, 0, 0);
-            }
-        }
+            for (int j = 0; j < 4; ++j) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][j], pb[j], acc[db], 0, 0, 0);
     };
 
     // ---- main loop: two tiles per trip so each buffer index is an immediate ---
@@ -264,7 +303,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     }
 
     // ---- epilogue: normalise, gate, round, store ------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (!q_valid) return;
     uint16_t *op = static_cast<uint16_t *>(a.o) + base + (uint64_t)q_local * row_stride;
