@@ -62,6 +62,34 @@ def test_attention_peaky_softmax():
     compare(to_bits(o), oracle.attention_rows(q_bits, k_bits, v_bits, None, cu, SCALE), "attn peaky")
 
 
+def _ramp_inputs(n, h, total_rise_log2, seed):
+    """Q rows all near one direction u and K rows (1 + r*i/n) * u: the logits in
+    log2 units move by about ``total_rise_log2`` from the first key to the last."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((h, 128)).astype(np.float32)
+    q = u[None] + 0.05 * rng.standard_normal((n, h, 128)).astype(np.float32)
+    c = SCALE * np.log2(np.e) * float((u * u).sum(axis=1).mean())
+    r = total_rise_log2 / c
+    ramp = (1.0 + r * np.arange(n, dtype=np.float32) / n)[:, None, None]
+    k = ramp * u[None] + 0.05 * rng.standard_normal((n, h, 128)).astype(np.float32)
+    v = rng.standard_normal((n, h, 128)).astype(np.float32)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits(q), bits(k), bits(v)
+
+
+@pytest.mark.parametrize("rise", [40.0, -40.0])
+def test_attention_drifting_logits(rise):
+    """Rising logits: the running max moves every few tiles (rescales) and the tiles in
+    between carry probabilities up to 2^8 (the exact-max check without a rescale).
+    Falling logits: every later tile underflows against the first one's max."""
+    cu = segment_offsets([1000, 130])
+    n, h = cu[-1], 2
+    say("attention drifting logits", rise)
+    qb, kb, vb = _ramp_inputs(n, h, rise, seed=1301 if rise > 0 else 1302)
+    o, _ = _run(to_device(qb), to_device(kb), to_device(vb), None, cu)
+    compare(to_bits(o), oracle.attention_rows(qb, kb, vb, None, cu, SCALE), f"attn drifting {rise}")
+
+
 def test_attention_gate_zero_halves_exactly():
     cu = segment_offsets([200, 57])
     n, h = cu[-1], 2

@@ -24,7 +24,9 @@
 //   online softmax   base 2, log2(e) folded into the scale; the running max
 //                    is only raised when a row's new maximum exceeds it by
 //                    more than 2^8 (probabilities stay <= 256, exact in the
-//                    final normalisation), so the O rescale is rare;
+//                    final normalisation), so the O rescale is rare; the tile
+//                    max itself is only computed when a lane's partial row
+//                    sum shows a probability of 2^7 or more;
 //   O^T += V^T P^T   B = P^T straight from the S^T registers (the MFMA k
 //                    slots are assigned to keys in exactly the order the C
 //                    layout left them in), A = V^T read with the gfx950
@@ -72,6 +74,7 @@ constexpr int kTileElems = kBN * kD;     // one K or V tile
 constexpr int kWaves = kAttnThreads / 64;
 constexpr int kLoadsPerTile = kBN / (4 * kWaves);   // 16-byte direct loads per lane per operand
 constexpr float kLazyRescale = 8.0f;     // log2 of the largest tolerated probability
+constexpr float kMaxCheck = 128.0f;      // partial row sum that triggers the exact max (2^7 < 2^8)
 constexpr int kBufferWord3 = 0x00020000; // buffer resource word 3 for raw 32-bit data on gfx9-class parts
 constexpr int kSchedMfma = 0x008;        // sched_group_barrier class masks
 constexpr int kSchedDsRead = 0x100;
@@ -182,21 +185,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
     const int n_kt = (seg_len + kBN - 1) / kBN;
     const int row_bytes = (int)(row_stride * 2);       // <= 256 heads * 256 B
+    int ld_off[kLoadsPerTile];                          // byte offsets inside a full tile
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) ld_off[i] = (ld_row0 + 4 * kWaves * i) * row_bytes + ld_chunk * 16;
     auto issue_tile = [&](int kt, uint16_t *dk, uint16_t *dv) {
         const uint64_t tile0 = (uint64_t)kt * kBN * row_stride;
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void *)(kp + tile0), 0, kBN * row_bytes, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void *)(vp + tile0), 0, kBN * row_bytes, kBufferWord3);
-        const int last = seg_len - 1 - kt * kBN;          // last key of the segment, tile-relative
+        if ((kt + 1) * kBN <= seg_len) {
 #pragma unroll
-        for (int i = 0; i < kLoadsPerTile; ++i) {
-            int key = ld_row0 + 4 * kWaves * i;
-            key = key < last ? key : last;
-            const int off = key * row_bytes + ld_chunk * 16;
-            const int lds_row = 4 * (kWaves * i + wave);            // wave-uniform
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + lds_row * kD), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + lds_row * kD), 16, off, 0, 0, 0);
+            for (int i = 0; i < kLoadsPerTile; ++i) {
+                const int lds_row = 4 * (kWaves * i + wave);            // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + lds_row * kD), 16, ld_off[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + lds_row * kD), 16, ld_off[i], 0, 0, 0);
+            }
+        } else {
+            // last tile of the segment: rows past its end re-read the last row
+            const int last = seg_len - 1 - kt * kBN;
+#pragma unroll
+            for (int i = 0; i < kLoadsPerTile; ++i) {
+                int key = ld_row0 + 4 * kWaves * i;
+                key = key < last ? key : last;
+                const int off = key * row_bytes + ld_chunk * 16;
+                const int lds_row = 4 * (kWaves * i + wave);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk + lds_row * kD), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv + lds_row * kD), 16, off, 0, 0, 0);
+            }
         }
     };
 
@@ -249,35 +265,47 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
                     if (key >= seg_len) s[kb][r] = -__builtin_inff();
                 }
         }
-        // online softmax (base 2) with lazy rescaling
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-        mx = half_max(mx) * a.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
-            const float m_new = __builtin_fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
-            m_run = m_new;
-        }
-        float psum = 0.f;
+        // online softmax (base 2) with lazy rescaling.  The probabilities are first
+        // formed against the running max.  A probability of 2^7 or more, or the
+        // NaN/inf of the first tile (running max still -inf), makes that lane's
+        // partial row sum reach 2^7 or fail the comparison; only then is the tile
+        // max computed, and only if it exceeds the running max by more than 2^8 are
+        // the accumulators rescaled and the probabilities formed again.
+        float psum;
         bf16x8 pb[4];
+        auto form_p = [&]() {
+            psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kb = j >> 1, r0 = (j & 1) * 8;
-            uint32_t wds[4];
+            for (int j = 0; j < 4; ++j) {
+                const int kb = j >> 1, r0 = (j & 1) * 8;
+                uint32_t wds[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e], a.scale_log2, -m_run));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e + 1], a.scale_log2, -m_run));
-                wds[e] = pack_bf16x2(p0, p1);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wds[e]), ones, psum, false);
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e], a.scale_log2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + 2 * e + 1], a.scale_log2, -m_run));
+                    wds[e] = pack_bf16x2(p0, p1);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wds[e]), ones, psum, false);
+                }
+                pb[j] = __builtin_bit_cast(bf16x8, (u32x4){wds[0], wds[1], wds[2], wds[3]});
             }
-            pb[j] = __builtin_bit_cast(bf16x8, (u32x4){wds[0], wds[1], wds[2], wds[3]});
+        };
+        form_p();
+        if (__builtin_amdgcn_ballot_w64(!(psum < kMaxCheck)) != 0) {
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+            mx = half_max(mx) * a.scale_log2;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+                const float m_new = __builtin_fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
+                m_run = m_new;
+                form_p();
+            }
         }
         l_run += psum;
 
