@@ -10,7 +10,9 @@ ranks, one rank's share of 14 heads.
 
 Prints ONE JSON line.  ``value`` is the packed-attention throughput in TFLOP/s
 (algorithmic FLOPs of the step's attention / time of its attention launch);
-relayout and AdaLN rates are reported under ``components``.  ``roofline``
+relayout and AdaLN rates are reported under ``components``; the relayout
+adjoints of the backward pass, timed after the step, under ``backward``.
+``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on this host's cores.
@@ -126,6 +128,46 @@ def cpu_baseline(step, workload, budget_s: float):
     }
 
 
+def measure_backward(step, reps: int = 5) -> dict:
+    """The relayout adjoints (backward of seq2head and head2seq) at the same
+    workload and plan, timed with HIP events after the timed steps.  They are
+    reported beside the step, not folded into ``value``."""
+    import torch
+
+    import ulysses_layout_amd as h3
+
+    grad_src = torch.empty_like(step.qkv)                 # [N, K, H, D] gradient of the packed operand
+    st = torch.cuda.current_stream()
+
+    def s2h_bwd():
+        return h3.seq2head_backward(step.rank_bufs, grad_src, step.world, rank=step.relayout_rank,
+                                    max_chunk_bytes=step.max_chunk_bytes, stream=st)
+
+    def h2s_bwd():
+        return h3.head2seq_backward(step.out, step.attn_out, step.world, rank=step.head2seq_rank,
+                                    max_chunk_bytes=step.max_chunk_bytes, stream=st)
+
+    rb = step.relayout_bytes()
+    out = {}
+    for name, fn, nbytes in (("seq2head_backward", s2h_bwd, rb["seq2head"]), ("head2seq_backward", h2s_bwd,
+                                                                                rb["head2seq"])):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        plan = None
+        for a, b in ev:
+            a.record(st)
+            plan = fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes,
+                     "launches": plan.launches}
+    del grad_src
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -185,6 +227,7 @@ def main():
     flops_per_launch = attn_flops / attn_launches
     launch_ms = ms["attention"] / attn_launches
     traffic = read_traffic(flops_per_launch)
+    backward = measure_backward(step)
 
     components = {
         "seq2head": {"ms": ms["seq2head"], "GBps": s2h_gbps, "frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
@@ -227,6 +270,7 @@ def main():
         "relayout_frac_hbm": (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3)
         / 1e9 / PEAK_HBM_GBPS,
         "components": components,
+        "backward": backward,
         "roofline": {
             "kernel": ATTN_KERNEL,
             "bound": "mfma",

@@ -129,6 +129,39 @@ h3_status h3_head2seq(const h3_layout *layout, const void *const *src, void *dst
                       void *stream, h3_plan_info *info);
 
 /* ------------------------------------------------------------------------
+ * h3_seq2head_backward -- the adjoint of h3_seq2head, for the backward pass
+ * ([PR] Problem and behavior: backward reuses the plan its forward saved;
+ * [PR] Review and validation: the native gate checks exact gradients).
+ *
+ * The relayout is a permutation, so its adjoint is the inverse copy:
+ *   grad_src[t][p][hb_j + h][:] = grad_dst[j*K + p][t][h][:], bit for bit,
+ * for every selected rank j and plane p.
+ * layout: the forward call's layout, unchanged.  The call derives its chunk
+ *      plan from it exactly as the forward does, so `info` reports the same
+ *      launches, chunks, chunk_tokens, grid and block as the forward's.
+ * grad_dst: host array of P*K device pointers, [N][H_j][D] each (the
+ *      gradients of the forward's dst buffers); with layout->rank = j only
+ *      the K entries of rank j are read and the others may be NULL.
+ * grad_src: device, [N][K][H][D].  Heads of unselected ranks are left
+ *      untouched (they belong to other ranks' shares).
+ * Launches: K * chunks, in plane order.  Errors as h3_seq2head.
+ * ------------------------------------------------------------------------ */
+h3_status h3_seq2head_backward(const h3_layout *layout, const void *const *grad_dst, void *grad_src,
+                               void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_head2seq_backward -- the adjoint of h3_head2seq (same passages):
+ *   grad_src[j][t][h][:] = grad_dst[t][hb_j + h][:] for every selected rank j.
+ * layout: the forward call's layout (n_planes = 1); the chunk plan and the
+ *      reported info equal the forward's.
+ * grad_dst: device, [N][H][D].  grad_src: host array of P device pointers,
+ *      [N][H_j][D] each; with layout->rank = j only grad_src[j] is written.
+ * Launches: chunks.  Errors as h3_head2seq.
+ * ------------------------------------------------------------------------ */
+h3_status h3_head2seq_backward(const h3_layout *layout, const void *grad_dst, void *const *grad_src,
+                               void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
  * h3_packed_attn -- segment-masked attention over the packed sequence, for
  * the heads one rank holds after seq2head ([DIST] introduction: attention on
  * the whole native packed sequence, no semantic padding).

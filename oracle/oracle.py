@@ -22,6 +22,11 @@ for a reader to check against the pages by eye:
                         Harden Ulysses agreement and tune bounded H3
                         transfers", Problem and behavior: one operand plane at
                         a time, outputs in storage of their own).
+* ``seq2head_backward`` / ``head2seq_backward`` -- the same exchanges run
+                        backwards: each message's gradient returns along its
+                        edge ("[perf] Harden Ulysses ...", Problem and behavior:
+                        backward reuses the forward's plan; Review and
+                        validation: exact gradients).
 * ``attention_rows`` -- segment-masked softmax attention in fp64 (C, threads).
 * ``attention_dense`` -- the same result reached a second way: one dense
                         N x N logit matrix with -inf off the segment blocks.
@@ -197,6 +202,55 @@ def head2seq(bufs: Sequence[np.ndarray], n_heads: int) -> np.ndarray:
     return np.concatenate(shards, axis=0)
 
 
+def seq2head_backward(grads: dict, n_tokens: int, n_planes: int, n_heads: int, world: int,
+                      ranks: Optional[Sequence[int]] = None, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Backward of ``seq2head``: every message's gradient travels back along its edge.
+
+    In the forward exchange rank ``i`` sent rank ``j`` the message
+    ``src[a_i:b_i, p, hb_j:hb_j+H_j, :]`` and rank ``j`` stacked the messages in
+    source-rank order.  The backward pass ("[perf] Harden Ulysses agreement
+    ...", Problem and behavior: backward reuses the plan of its forward; Review
+    and validation: exact gradients) therefore cuts rank ``j``'s gradient
+    ``grads[(j, p)]`` (``[N, H_j, D]``) back into the same messages and rank
+    ``i`` writes each one where its forward message came from.
+
+    Returns the ``[N, K, H, D]`` gradient of the packed operand.  Heads of ranks
+    outside ``ranks`` keep the values of ``out`` (zeros when ``out`` is None).
+    """
+    d = next(iter(grads.values())).shape[2]
+    tokens = partition(n_tokens, world)
+    heads = partition(n_heads, world)
+    ranks = range(world) if ranks is None else ranks
+    res = (np.zeros((n_tokens, n_planes, n_heads, d), dtype=next(iter(grads.values())).dtype)
+           if out is None else np.array(out, copy=True))
+    for p in range(n_planes):
+        for j in ranks:
+            hb, hn = heads[j]
+            g = grads[(j, p)]
+            if g.shape != (n_tokens, hn, d):
+                raise ValueError(f"gradient of rank {j}, plane {p} has shape {g.shape}, expected {(n_tokens, hn, d)}")
+            for i in range(world):
+                a, cnt = tokens[i]
+                res[a:a + cnt, p, hb:hb + hn, :] = g[a:a + cnt]
+    return res
+
+
+def head2seq_backward(grad: np.ndarray, world: int, ranks: Optional[Sequence[int]] = None) -> dict:
+    """Backward of ``head2seq``: rank ``i`` sends rank ``j`` the gradient of the
+    rows it received from ``j`` -- heads ``[hb_j, hb_j+H_j)`` of its own token
+    shard -- and rank ``j`` stacks them in rank order.  Returns ``{j: [N, H_j, D]}``.
+    """
+    n, n_heads, d = grad.shape
+    tokens = partition(n, world)
+    heads = partition(n_heads, world)
+    ranks = range(world) if ranks is None else ranks
+    res = {}
+    for j in ranks:
+        hb, hn = heads[j]
+        res[j] = np.concatenate([grad[a:a + cnt, hb:hb + hn, :] for a, cnt in tokens], axis=0)
+    return res
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
@@ -324,6 +378,7 @@ def attention_flops(cu: Sequence[int], n_heads: int, head_dim: int) -> int:
     return 4 * head_dim * n_heads * sum((int(cu[s + 1]) - int(cu[s])) ** 2 for s in range(len(cu) - 1))
 
 
-__all__ = ["build", "partition", "clip_segments", "seq2head", "head2seq", "attention_rows",
+__all__ = ["build", "partition", "clip_segments", "seq2head", "head2seq", "seq2head_backward",
+           "head2seq_backward", "attention_rows",
            "attention_dense", "adaln_rows", "bf16_bits_to_f64", "EmptyPartition", "MODULATE",
            "GATE_RESIDUAL", "default_threads", "attention_flops"]

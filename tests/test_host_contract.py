@@ -149,6 +149,70 @@ def test_seq2head_rejects_null_and_alias():
     assert rc == ARG
 
 
+def _seq2head_bwd(layout, grad_src=FAKE, grad_dst=None):
+    k, p = layout.n_planes, layout.world
+    if grad_dst is None:
+        heads = [c for _, c in oracle.partition(layout.n_heads, p)] if 1 <= p <= layout.n_heads else []
+        grad_dst, addr = [], FAKE * 2
+        for j in range(max(p, 0)):
+            for _ in range(k):
+                grad_dst.append(addr)
+                addr += layout.n_tokens * (heads[j] if heads else 1) * 256 + 4096
+    arr = (ctypes.c_void_p * max(len(grad_dst), 1))(*grad_dst)
+    info = _PlanInfo()
+    return LIB.h3_seq2head_backward(ctypes.byref(layout), arr, grad_src, None, ctypes.byref(info)), info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(world=0), EMPTY), (dict(world=57), EMPTY), (dict(n_tokens=0), EMPTY), (dict(head_dim=64), UNSUP),
+    (dict(n_planes=9), ARG), (dict(rank=2), ARG), (dict(max_chunk_bytes=1000), ARG),
+])
+def test_seq2head_backward_rejects_bad_layout(kw, status):
+    rc, info = _seq2head_bwd(_layout(**kw))
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+    assert LIB.h3_last_error().decode()
+
+
+def test_seq2head_backward_rejects_null_and_alias():
+    lay = _layout()
+    assert _seq2head_bwd(lay, grad_src=None)[0] == ARG
+    gd = [FAKE * 2 + i * (1 << 24) for i in range(6)]
+    gd[2] = None
+    assert _seq2head_bwd(lay, grad_dst=gd)[0] == ARG
+    # a gradient input inside the output
+    gd = [FAKE * 2 + i * (1 << 24) for i in range(6)]
+    gd[0] = FAKE + 4096
+    assert _seq2head_bwd(lay, grad_dst=gd)[0] == ALIAS
+
+
+def _head2seq_bwd(layout, grad_dst=FAKE, grad_src=None):
+    p = layout.world
+    if grad_src is None:
+        grad_src = [FAKE * 2 + j * (1 << 28) for j in range(max(p, 0))]
+    arr = (ctypes.c_void_p * max(len(grad_src), 1))(*grad_src)
+    info = _PlanInfo()
+    return LIB.h3_head2seq_backward(ctypes.byref(layout), grad_dst, arr, None, ctypes.byref(info)), info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_planes=3), ARG), (dict(world=57), EMPTY), (dict(head_dim=64), UNSUP), (dict(rank=5), ARG),
+])
+def test_head2seq_backward_rejects_bad_layout(kw, status):
+    base = dict(n_planes=1)
+    base.update(kw)
+    rc, info = _head2seq_bwd(_layout(**base))
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+def test_head2seq_backward_rejects_null_and_alias():
+    lay = _layout(n_planes=1)
+    assert _head2seq_bwd(lay, grad_dst=None)[0] == ARG
+    assert _head2seq_bwd(lay, grad_src=[FAKE * 2, None])[0] == ARG
+    assert _head2seq_bwd(lay, grad_src=[FAKE * 2, FAKE + 256])[0] == ALIAS
+
+
 def test_rejected_call_leaves_no_state():
     rc, _ = _seq2head(_layout(world=57))
     assert rc == EMPTY

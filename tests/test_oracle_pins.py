@@ -193,6 +193,81 @@ def test_head2seq_elements_land_on_their_global_head():
     assert np.array_equal(out.reshape(-1), np.arange(n * h * d))
 
 
+# ---- backward of the relayouts ------------------------------------------------
+
+@pytest.mark.parametrize("world", [1, 2, 3, 6, 8])
+def test_seq2head_backward_is_the_adjoint(world):
+    """<seq2head(x), y> = <x, seq2head_backward(y)> exactly, on integer-valued data."""
+    rng = np.random.default_rng(40 + world)
+    n, k, h, d = 29, 3, 56, 4
+    x = rng.integers(-50, 50, size=(n, k, h, d)).astype(np.float64)
+    heads = oracle.partition(h, world)
+    y = {(j, p): rng.integers(-50, 50, size=(n, heads[j][1], d)).astype(np.float64)
+         for j in range(world) for p in range(k)}
+    fx = oracle.seq2head(x, world)
+    lhs = sum(float((fx[key] * y[key]).sum()) for key in y)
+    rhs = float((x * oracle.seq2head_backward(y, n, k, h, world)).sum())
+    assert lhs == rhs
+
+
+@pytest.mark.parametrize("world", [1, 2, 3, 6, 8])
+def test_seq2head_backward_matches_library_autograd(world):
+    """Gradient of the relayout written with torch.tensor_split (torch's own
+    quotient/remainder split) and taken by autograd."""
+    rng = np.random.default_rng(60 + world)
+    n, k, h, d = 17, 4, 56, 3
+    x = torch.tensor(rng.standard_normal((n, k, h, d)), dtype=torch.float64, requires_grad=True)
+    parts = torch.tensor_split(x, world, dim=2)
+    w = {(j, p): rng.standard_normal((n, parts[j].shape[2], d)) for j in range(world) for p in range(k)}
+    loss = sum((parts[j][:, p] * torch.from_numpy(w[(j, p)])).sum() for j in range(world) for p in range(k))
+    loss.backward()
+    assert np.array_equal(oracle.seq2head_backward(w, n, k, h, world), x.grad.numpy())
+
+
+def test_seq2head_backward_rank_share_and_round_trip():
+    src = normal_bf16_bits((33, 4, 56, 8), seed=13)
+    for world in (1, 4, 6):
+        fwd = oracle.seq2head(src, world)
+        assert np.array_equal(oracle.seq2head_backward(fwd, 33, 4, 56, world), src)
+        # one rank's share: its heads are written, the rest keep the initial values
+        j = world - 1
+        hb, hn = oracle.partition(56, world)[j]
+        init = np.full(src.shape, 7, np.uint16)
+        part = oracle.seq2head_backward({(j, p): fwd[(j, p)] for p in range(4)}, 33, 4, 56, world, ranks=[j],
+                                        out=init)
+        assert np.array_equal(part[:, :, hb:hb + hn], src[:, :, hb:hb + hn])
+        mask = np.ones(56, bool)
+        mask[hb:hb + hn] = False
+        assert (part[:, :, mask] == 7).all()
+
+
+@pytest.mark.parametrize("world", [1, 2, 5, 8])
+def test_head2seq_backward_matches_library_autograd(world):
+    """Gradient of head2seq written as torch.cat of the rank buffers along heads."""
+    rng = np.random.default_rng(80 + world)
+    n, h, d = 21, 56, 3
+    sizes = [t.shape[2] for t in torch.tensor_split(torch.empty(1, 1, h), world, dim=2)]
+    bufs = [torch.tensor(rng.standard_normal((n, c, d)), dtype=torch.float64, requires_grad=True) for c in sizes]
+    w = rng.standard_normal((n, h, d))
+    (torch.cat(bufs, dim=1) * torch.from_numpy(w)).sum().backward()
+    got = oracle.head2seq_backward(w, world)
+    for j in range(world):
+        assert np.array_equal(got[j], bufs[j].grad.numpy())
+
+
+def test_head2seq_backward_is_the_adjoint_and_inverts_head2seq():
+    rng = np.random.default_rng(91)
+    n, h, d, world = 26, 56, 4, 6
+    heads = oracle.partition(h, world)
+    bufs = [rng.integers(-9, 9, size=(n, hn, d)).astype(np.float64) for _, hn in heads]
+    y = rng.integers(-9, 9, size=(n, h, d)).astype(np.float64)
+    gb = oracle.head2seq_backward(y, world)
+    assert float((oracle.head2seq(bufs, h) * y).sum()) == sum(float((bufs[j] * gb[j]).sum()) for j in range(world))
+    back = oracle.head2seq_backward(oracle.head2seq(bufs, h), world)
+    for j in range(world):
+        assert np.array_equal(back[j], bufs[j])
+
+
 def test_head2seq_rejects_wrong_buffer_shape():
     bufs = [np.zeros((8, 28, 4), np.uint16), np.zeros((8, 27, 4), np.uint16)]
     with pytest.raises(ValueError):

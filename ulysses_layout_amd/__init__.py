@@ -1,4 +1,5 @@
-"""MI355X-native Ulysses H3 hot path: seq2head / packed attention / head2seq / AdaLN.
+"""MI355X-native Ulysses H3 hot path: seq2head / packed attention / head2seq / AdaLN,
+plus the adjoints of the two relayouts for the backward pass.
 
 The compute lives in ``libh3.so`` (hand-written HIP for gfx950, C ABI declared
 in ``include/h3.h``); this package is its thin ctypes binding.  Importing it
@@ -6,6 +7,6 @@ fails if the library has not been built.
 """
 from .h3 import (  # noqa: F401
     EXPORTS, H3_ADALN_GATE_RESIDUAL, H3_ADALN_MODULATE, HEAD_DIM, H3Error, Layout, PlanInfo,
-    adaln_segment, clip_segments, head2seq, head_split, library, packed_attn, partition, seq2head,
-    version,
+    adaln_segment, clip_segments, head2seq, head2seq_backward, head_split, library, packed_attn, partition,
+    seq2head, seq2head_backward, version,
 )

@@ -1,6 +1,8 @@
 """Build libh3.so in-tree: every HIP source compiled for gfx950 with hipcc.
 
-Usage: ``python -m ulysses_layout_amd.build`` (or ``build()`` from Python).
+Usage: ``python ulysses_layout_amd/build.py`` (or ``build()`` from Python after
+loading this file by path).  It is run as a file, not as a package module,
+because importing the package loads the library this script rebuilds.
 The objects go to ``ulysses_layout_amd/_build/`` and the shared library to
 ``ulysses_layout_amd/libh3.so``.  Every call recompiles every source.
 """

@@ -337,6 +337,160 @@ h3_status h3_head2seq(const h3_layout *L, const void *const *src, void *dst, voi
     return ok();
 }
 
+h3_status h3_seq2head_backward(const h3_layout *L, const void *const *grad_dst, void *grad_src, void *stream,
+                               h3_plan_info *info) {
+    // Adjoint of h3_seq2head: the rank -> packed copy, with the forward's packed
+    // stride (K planes) and the forward's chunk plan.
+    clear_info(info);
+    h3_status st = check_layout(L, false);
+    if (st != H3_OK) return st;
+    if (!grad_dst) return fail(H3_ERR_ARG, "grad_dst is NULL");
+    if (!grad_src) return fail(H3_ERR_ARG, "grad_src is NULL");
+    const int P = L->world, K = L->n_planes;
+    const int r0 = L->rank < 0 ? 0 : L->rank;
+    const int nr = L->rank < 0 ? P : 1;
+    const uint64_t row_bytes = (uint64_t)L->n_heads * L->head_dim * 2;
+
+    int64_t hb[h3::kMaxRanks], hn[h3::kMaxRanks];
+    for (int j = 0; j < P; ++j) split(L->n_heads, P, j, &hb[j], &hn[j]);
+    std::vector<Range> ins, outs{range_of(grad_src, (uint64_t)L->n_tokens * K * row_bytes, "grad_src", 0)};
+    for (int j = r0; j < r0 + nr; ++j)
+        for (int p = 0; p < K; ++p) {
+            if (!grad_dst[j * K + p])
+                return fail(H3_ERR_ARG, "grad_dst[%d] (rank %d, plane %d) is NULL", j * K + p, j, p);
+            ins.push_back(range_of(grad_dst[j * K + p], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "grad_dst",
+                                   j * K + p));
+        }
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+
+    const uint32_t vec_per_head = L->head_dim / 8;
+    const uint32_t stride_vec = (uint32_t)K * L->n_heads * vec_per_head;     // as the forward
+    int64_t chunk, user_chunk;
+    int32_t n_chunks;
+    plan_chunks(L, stride_vec, &chunk, &n_chunks, &user_chunk);
+
+    h3::RunCopyArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint32_t max_run = 0;
+    uint64_t rank_bytes = 0;
+    for (int y = 0; y < nr; ++y) {
+        const int j = r0 + y;
+        a.run_vec[y] = (uint32_t)hn[j] * vec_per_head;
+        a.off_vec[y] = (uint32_t)hb[j] * vec_per_head;
+        a.div[y] = h3::make_fastdiv(a.run_vec[y]);
+        max_run = std::max(max_run, a.run_vec[y]);
+        rank_bytes += (uint64_t)hn[j] * L->head_dim * 2;
+    }
+    a.stride_vec = stride_vec;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int launches = 0, grid_max = 0;
+    for (int p = 0; p < K; ++p) {
+        for (int c = 0; c < n_chunks; ++c) {
+            const int64_t t0 = (int64_t)c * chunk;
+            const int64_t nt = std::min<int64_t>(chunk, L->n_tokens - t0);
+            a.dst_packed = static_cast<char *>(grad_src) + ((uint64_t)t0 * K + p) * row_bytes;
+            for (int y = 0; y < nr; ++y) {
+                const int j = r0 + y;
+                a.src_rank[y] = static_cast<const char *>(grad_dst[j * K + p]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
+            }
+            a.n_tokens = (uint32_t)nt;
+            int gx = 0;
+            hipError_t e = h3::launch_head2seq(a, nr, max_run, s, &gx);
+            if (e != hipSuccess)
+                return fail(H3_ERR_HIP, "seq2head backward launch (plane %d, chunk %d) failed: %s", p, c,
+                            hipGetErrorString(e));
+            ++launches;
+            grid_max = std::max(grid_max, gx);
+        }
+    }
+    if (info) {
+        info->launches = launches;
+        info->chunks = n_chunks;
+        info->grid_x = grid_max;
+        info->block_x = h3::kCopyThreads;
+        info->chunk_tokens = chunk;
+        info->max_launch_src_bytes = (int64_t)(std::min<int64_t>(chunk, L->n_tokens) * rank_bytes);
+        info->bytes_read = (int64_t)((uint64_t)L->n_tokens * K * rank_bytes);
+        info->bytes_written = info->bytes_read;
+    }
+    return ok();
+}
+
+h3_status h3_head2seq_backward(const h3_layout *L, const void *grad_dst, void *const *grad_src, void *stream,
+                               h3_plan_info *info) {
+    // Adjoint of h3_head2seq: the packed -> rank copy of one plane, with the
+    // forward's chunk plan.
+    clear_info(info);
+    h3_status st = check_layout(L, true);
+    if (st != H3_OK) return st;
+    if (!grad_dst) return fail(H3_ERR_ARG, "grad_dst is NULL");
+    if (!grad_src) return fail(H3_ERR_ARG, "grad_src is NULL");
+    const int P = L->world;
+    const int r0 = L->rank < 0 ? 0 : L->rank;
+    const int nr = L->rank < 0 ? P : 1;
+    const uint64_t row_bytes = (uint64_t)L->n_heads * L->head_dim * 2;
+
+    int64_t hb[h3::kMaxRanks], hn[h3::kMaxRanks];
+    for (int j = 0; j < P; ++j) split(L->n_heads, P, j, &hb[j], &hn[j]);
+    std::vector<Range> ins{range_of(grad_dst, (uint64_t)L->n_tokens * row_bytes, "grad_dst", 0)}, outs;
+    for (int j = r0; j < r0 + nr; ++j) {
+        if (!grad_src[j]) return fail(H3_ERR_ARG, "grad_src[%d] is NULL", j);
+        outs.push_back(range_of(grad_src[j], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "grad_src", j));
+    }
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+
+    const uint32_t vec_per_head = L->head_dim / 8;
+    const uint32_t stride_vec = (uint32_t)L->n_heads * vec_per_head;           // as the forward
+    int64_t chunk, user_chunk;
+    int32_t n_chunks;
+    plan_chunks(L, stride_vec, &chunk, &n_chunks, &user_chunk);
+
+    h3::RunCopyArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint32_t max_run = 0;
+    uint64_t rank_bytes = 0;
+    for (int y = 0; y < nr; ++y) {
+        const int j = r0 + y;
+        a.run_vec[y] = (uint32_t)hn[j] * vec_per_head;
+        a.off_vec[y] = (uint32_t)hb[j] * vec_per_head;
+        a.div[y] = h3::make_fastdiv(a.run_vec[y]);
+        max_run = std::max(max_run, a.run_vec[y]);
+        rank_bytes += (uint64_t)hn[j] * L->head_dim * 2;
+    }
+    a.stride_vec = stride_vec;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int launches = 0, grid_max = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t t0 = (int64_t)c * chunk;
+        const int64_t nt = std::min<int64_t>(chunk, L->n_tokens - t0);
+        a.src_packed = static_cast<const char *>(grad_dst) + (uint64_t)t0 * row_bytes;
+        for (int y = 0; y < nr; ++y) {
+            const int j = r0 + y;
+            a.dst_rank[y] = static_cast<char *>(grad_src[j]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
+        }
+        a.n_tokens = (uint32_t)nt;
+        int gx = 0;
+        hipError_t e = h3::launch_seq2head(a, nr, max_run, s, &gx);
+        if (e != hipSuccess)
+            return fail(H3_ERR_HIP, "head2seq backward launch (chunk %d) failed: %s", c, hipGetErrorString(e));
+        ++launches;
+        grid_max = std::max(grid_max, gx);
+    }
+    if (info) {
+        info->launches = launches;
+        info->chunks = n_chunks;
+        info->grid_x = grid_max;
+        info->block_x = h3::kCopyThreads;
+        info->chunk_tokens = chunk;
+        info->max_launch_src_bytes = (int64_t)(std::min<int64_t>(chunk, L->n_tokens) * rank_bytes);
+        info->bytes_read = (int64_t)((uint64_t)L->n_tokens * rank_bytes);
+        info->bytes_written = info->bytes_read;
+    }
+    return ok();
+}
+
 h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void *g, void *o, int64_t n_tokens,
                          int32_t n_heads, int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale,
                          void *stream, h3_plan_info *info) {

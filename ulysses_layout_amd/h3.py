@@ -25,8 +25,9 @@ STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3
                 4: "H3_ERR_UNSUPPORTED", 5: "H3_ERR_ALIAS", 6: "H3_ERR_HIP"}
 
 # names every build of libh3.so must export (the declarations of include/h3.h)
-EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_packed_attn", "h3_adaln_segment", "h3_partition",
-           "h3_clip_segments", "h3_status_string", "h3_last_error", "h3_version")
+EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
+           "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
+           "h3_version")
 
 
 class H3Error(RuntimeError):
@@ -66,21 +67,28 @@ class PlanInfo:
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ulysses_layout_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python ulysses_layout_amd/build.py` "
                           "(the hot path has no other implementation)")
     lib = ctypes.CDLL(LIB_PATH)
+    missing = [name for name in EXPORTS if not hasattr(lib, name)]
+    if missing:
+        raise ImportError(f"{LIB_PATH} is stale (does not export {', '.join(missing)}): rebuild it with "
+                          "`python ulysses_layout_amd/build.py`")
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     i64p = ctypes.POINTER(ctypes.c_int64)
     lp = ctypes.POINTER(Layout)
     ip = ctypes.POINTER(_PlanInfo)
     lib.h3_seq2head.argtypes = [lp, vp, ctypes.POINTER(vp), vp, ip]
     lib.h3_head2seq.argtypes = [lp, ctypes.POINTER(vp), vp, vp, ip]
+    lib.h3_seq2head_backward.argtypes = [lp, ctypes.POINTER(vp), vp, vp, ip]
+    lib.h3_head2seq_backward.argtypes = [lp, vp, ctypes.POINTER(vp), vp, ip]
     lib.h3_packed_attn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_adaln_segment.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, i64p, i32, f32, vp, ip]
     lib.h3_partition.argtypes = [i64, i32, i32, i64p, i64p]
     lib.h3_clip_segments.argtypes = [i64p, i32, i64, i64, ctypes.POINTER(i32), i64p, i64p]
     lib.h3_clip_segments.restype = i32
-    for name in ("h3_seq2head", "h3_head2seq", "h3_packed_attn", "h3_adaln_segment", "h3_partition"):
+    for name in ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward",
+                 "h3_packed_attn", "h3_adaln_segment", "h3_partition"):
         getattr(lib, name).restype = ctypes.c_int
     lib.h3_status_string.argtypes = [ctypes.c_int]
     lib.h3_status_string.restype = ctypes.c_char_p
@@ -211,6 +219,46 @@ def head2seq(src: Sequence, dst, world: int, rank: int = -1, max_chunk_bytes: in
     lay = Layout(n, h, d, 1, world, rank, 0, max_chunk_bytes)
     info = _PlanInfo()
     _check(_lib.h3_head2seq(ctypes.byref(lay), ptrs, dst_ptr, _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def seq2head_backward(grad_dst: Sequence[Sequence], grad_src, world: int, rank: int = -1,
+                      max_chunk_bytes: int = 0, stream=None) -> PlanInfo:
+    """Adjoint of ``seq2head``: ``grad_dst[j][p]`` [N, H_j, 128] -> ``grad_src`` [N, K, H, 128].
+
+    Takes the forward call's ``world``, ``rank`` and ``max_chunk_bytes``; the
+    returned plan equals the forward's.  Heads of unselected ranks in
+    ``grad_src`` are left untouched.
+    """
+    n, k, h, d = grad_src.shape
+    gs_ptr = _dev_bf16(grad_src, "grad_src")
+    ptrs = (ctypes.c_void_p * (world * k))()
+    heads = head_split(h, world) if 1 <= world <= h else [(0, 0)] * max(world, 0)
+    for j in range(world):
+        if rank not in (-1, j):
+            continue
+        for p in range(k):
+            ptrs[j * k + p] = _dev_bf16(grad_dst[j][p], f"grad_dst[{j}][{p}]", (n, heads[j][1], d))
+    lay = Layout(n, h, d, k, world, rank, 0, max_chunk_bytes)
+    info = _PlanInfo()
+    _check(_lib.h3_seq2head_backward(ctypes.byref(lay), ptrs, gs_ptr, _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def head2seq_backward(grad_dst, grad_src: Sequence, world: int, rank: int = -1, max_chunk_bytes: int = 0,
+                      stream=None) -> PlanInfo:
+    """Adjoint of ``head2seq``: ``grad_dst`` [N, H, 128] -> ``grad_src[j]`` [N, H_j, 128]."""
+    n, h, d = grad_dst.shape
+    gd_ptr = _dev_bf16(grad_dst, "grad_dst")
+    ptrs = (ctypes.c_void_p * world)()
+    heads = head_split(h, world) if 1 <= world <= h else [(0, 0)] * max(world, 0)
+    for j in range(world):
+        if rank not in (-1, j):
+            continue
+        ptrs[j] = _dev_bf16(grad_src[j], f"grad_src[{j}]", (n, heads[j][1], d))
+    lay = Layout(n, h, d, 1, world, rank, 0, max_chunk_bytes)
+    info = _PlanInfo()
+    _check(_lib.h3_head2seq_backward(ctypes.byref(lay), gd_ptr, ptrs, _stream_ptr(stream), ctypes.byref(info)))
     return _info(info)
 
 
