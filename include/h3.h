@@ -184,6 +184,21 @@ h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void
                          void *stream, h3_plan_info *info);
 
 /* ------------------------------------------------------------------------
+ * h3_packed_attn_lse -- h3_packed_attn that also writes the per-row
+ * log-sum-exp the backward pass needs (same passages; training forward).
+ *
+ * lse: device, fp32 [N][H] (N = n_tokens, H = n_heads), written for every
+ *      token and head: lse[t,h] = ln sum_{u in seg(t)} exp(scale * <q[t,h,:], k[u,h,:]>),
+ *      the normaliser of the softmax before the gate.  Must not overlap any
+ *      other buffer.  NULL is rejected (use h3_packed_attn).
+ * Everything else, including o, launches and errors, as h3_packed_attn.
+ * ------------------------------------------------------------------------ */
+h3_status h3_packed_attn_lse(const void *q, const void *k, const void *v, const void *g, void *o, float *lse,
+                             int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                             const int64_t *cu_seqlens, int32_t n_segments, float scale,
+                             void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
  * h3_adaln_segment -- per-segment AdaLN on one rank's token interval.
  *
  * [DIST] Partition Contract: segment boundaries are clipped to the rank's

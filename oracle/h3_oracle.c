@@ -139,6 +139,220 @@ static int run_threads(void *(*fn)(void *), void *job, int32_t n_threads) {
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Backward of the segment-masked, optionally gated attention above.        */
+/*                                                                          */
+/* With z_tu = scale*<q_t,k_u> over the keys u of t's segment,              */
+/* p_tu = exp(z_tu - lse_t), lse_t = ln sum_u exp(z_tu), the ungated row    */
+/* a_t = sum_u p_tu v_u and the output o_t = a_t * sig(g_t) (sig = 1 when   */
+/* there is no gate), the chain rule for an incoming gradient do_t gives:   */
+/*   e_t   = do_t * sig(g_t)               (gradient reaching a_t)         */
+/*   dg_t  = do_t * a_t * sig(g_t) * (1 - sig(g_t))                          */
+/*   D_t   = <e_t, a_t>                                                     */
+/*   ds_tu = p_tu * (<e_t, v_u> - D_t)     (softmax Jacobian)               */
+/*   dq_t  = scale * sum_u ds_tu k_u                                        */
+/*   dk_u  = scale * sum_t ds_tu q_t,   dv_u = sum_t p_tu e_t               */
+/* The query-side terms of one row need only that row; the key-side terms  */
+/* of one key need lse_t and D_t of every query t of its segment.          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *q, *k, *v, *g, *dout;
+    int64_t n_tokens;
+    int32_t n_heads, head_dim;
+    const int64_t *cu;
+    int32_t n_seg;
+    double scale;
+    const int64_t *rows;        /* query rows (row pass) or key rows (key pass) */
+    int64_t n_rows;
+    double *lse, *delta;        /* row pass: outputs [n_rows][H]; key pass: inputs [n_tokens][H] */
+    double *dq, *dg;            /* row pass: [n_rows][H][D] (dg may be NULL) */
+    double *dk, *dv;            /* key pass: [n_rows][H][D] */
+    int64_t next_task;
+    pthread_mutex_t lock;
+    int status;
+} bwd_job;
+
+static double sig(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* query-side terms of row r (token t), head h */
+static void bwd_row_one(const bwd_job *J, int64_t r, int32_t h, double *z, double *qrow, double *a, double *e) {
+    const int32_t D = J->head_dim, H = J->n_heads;
+    const int64_t t = J->rows[r];
+    const int32_t s = segment_of(J->cu, J->n_seg, t);
+    const int64_t lo = J->cu[s], hi = J->cu[s + 1];
+    for (int32_t d = 0; d < D; ++d) qrow[d] = bf16_bits_to_double(J->q[(t * H + h) * D + d]);
+    double zmax = -INFINITY;
+    for (int64_t u = lo; u < hi; ++u) {
+        double dot = 0.0;
+        const uint16_t *krow = J->k + (u * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) dot += qrow[d] * bf16_bits_to_double(krow[d]);
+        z[u - lo] = J->scale * dot;
+        if (z[u - lo] > zmax) zmax = z[u - lo];
+    }
+    double denom = 0.0;
+    for (int64_t u = lo; u < hi; ++u) denom += exp(z[u - lo] - zmax);
+    const double lse = zmax + log(denom);
+    /* a_t and e_t */
+    for (int32_t d = 0; d < D; ++d) a[d] = 0.0;
+    for (int64_t u = lo; u < hi; ++u) {
+        const double p = exp(z[u - lo] - lse);
+        const uint16_t *vrow = J->v + (u * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) a[d] += p * bf16_bits_to_double(vrow[d]);
+    }
+    double delta = 0.0;
+    for (int32_t d = 0; d < D; ++d) {
+        const double dov = bf16_bits_to_double(J->dout[(t * H + h) * D + d]);
+        const double sg = J->g ? sig(bf16_bits_to_double(J->g[(t * H + h) * D + d])) : 1.0;
+        e[d] = dov * sg;
+        if (J->dg) J->dg[(r * H + h) * D + d] = J->g ? dov * a[d] * sg * (1.0 - sg) : 0.0;
+        delta += e[d] * a[d];
+    }
+    J->lse[r * H + h] = lse;
+    J->delta[r * H + h] = delta;
+    /* dq_t = scale * sum_u p_tu (<e_t, v_u> - D_t) k_u */
+    double *dq = J->dq + (r * H + h) * D;
+    for (int32_t d = 0; d < D; ++d) dq[d] = 0.0;
+    for (int64_t u = lo; u < hi; ++u) {
+        const double p = exp(z[u - lo] - lse);
+        const uint16_t *vrow = J->v + (u * H + h) * D;
+        double dp = 0.0;
+        for (int32_t d = 0; d < D; ++d) dp += e[d] * bf16_bits_to_double(vrow[d]);
+        const double ds = p * (dp - delta);
+        const uint16_t *krow = J->k + (u * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) dq[d] += J->scale * ds * bf16_bits_to_double(krow[d]);
+    }
+}
+
+/* key-side terms of key row r (token u), head h; lse and delta hold every token's values */
+static void bwd_key_one(const bwd_job *J, int64_t r, int32_t h, double *krow, double *vrow) {
+    const int32_t D = J->head_dim, H = J->n_heads;
+    const int64_t u = J->rows[r];
+    const int32_t s = segment_of(J->cu, J->n_seg, u);
+    const int64_t lo = J->cu[s], hi = J->cu[s + 1];
+    for (int32_t d = 0; d < D; ++d) {
+        krow[d] = bf16_bits_to_double(J->k[(u * H + h) * D + d]);
+        vrow[d] = bf16_bits_to_double(J->v[(u * H + h) * D + d]);
+    }
+    double *dk = J->dk + (r * H + h) * D, *dv = J->dv + (r * H + h) * D;
+    for (int32_t d = 0; d < D; ++d) dk[d] = dv[d] = 0.0;
+    for (int64_t t = lo; t < hi; ++t) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += bf16_bits_to_double(J->q[(t * H + h) * D + d]) * krow[d];
+        const double p = exp(J->scale * dot - J->lse[t * H + h]);
+        double dp = 0.0;
+        for (int32_t d = 0; d < D; ++d) {
+            const double dov = bf16_bits_to_double(J->dout[(t * H + h) * D + d]);
+            const double sg = J->g ? sig(bf16_bits_to_double(J->g[(t * H + h) * D + d])) : 1.0;
+            const double ed = dov * sg;
+            dv[d] += p * ed;
+            dp += ed * vrow[d];
+        }
+        const double ds = p * (dp - J->delta[t * H + h]);
+        for (int32_t d = 0; d < D; ++d) dk[d] += J->scale * ds * bf16_bits_to_double(J->q[(t * H + h) * D + d]);
+    }
+}
+
+static void *bwd_row_worker(void *arg) {
+    bwd_job *J = (bwd_job *)arg;
+    int64_t longest = 0;
+    for (int32_t s = 0; s < J->n_seg; ++s)
+        if (J->cu[s + 1] - J->cu[s] > longest) longest = J->cu[s + 1] - J->cu[s];
+    double *z = (double *)malloc(sizeof(double) * (size_t)(longest > 0 ? longest : 1));
+    double *buf = (double *)malloc(sizeof(double) * 3 * (size_t)J->head_dim);
+    if (!z || !buf) {
+        pthread_mutex_lock(&J->lock);
+        J->status = -2;
+        pthread_mutex_unlock(&J->lock);
+        free(z); free(buf);
+        return NULL;
+    }
+    const int64_t total = J->n_rows * J->n_heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t task = J->next_task++;
+        pthread_mutex_unlock(&J->lock);
+        if (task >= total) break;
+        bwd_row_one(J, task / J->n_heads, (int32_t)(task % J->n_heads), z, buf, buf + J->head_dim,
+                    buf + 2 * J->head_dim);
+    }
+    free(z); free(buf);
+    return NULL;
+}
+
+static void *bwd_key_worker(void *arg) {
+    bwd_job *J = (bwd_job *)arg;
+    double *buf = (double *)malloc(sizeof(double) * 2 * (size_t)J->head_dim);
+    if (!buf) {
+        pthread_mutex_lock(&J->lock);
+        J->status = -2;
+        pthread_mutex_unlock(&J->lock);
+        return NULL;
+    }
+    const int64_t total = J->n_rows * J->n_heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t task = J->next_task++;
+        pthread_mutex_unlock(&J->lock);
+        if (task >= total) break;
+        bwd_key_one(J, task / J->n_heads, (int32_t)(task % J->n_heads), buf, buf + J->head_dim);
+    }
+    free(buf);
+    return NULL;
+}
+
+static int bwd_check(const int64_t *cu, int32_t n_seg, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                     const int64_t *rows, int64_t n_rows) {
+    if (n_seg < 1 || n_heads < 1 || head_dim < 1 || !cu || cu[0] != 0 || cu[n_seg] != n_tokens) return -1;
+    for (int32_t s = 0; s < n_seg; ++s)
+        if (cu[s + 1] <= cu[s]) return -1;
+    if (n_rows > 0 && !rows) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= n_tokens) return -1;
+    return 0;
+}
+
+/* Query-side pass: lse, delta [n_rows][H]; dq, dg [n_rows][H][D] (dg NULL when g is NULL). */
+int h3o_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                      const uint16_t *dout, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                      const int64_t *cu, int32_t n_seg, double scale, const int64_t *rows, int64_t n_rows,
+                      double *lse, double *delta, double *dq, double *dg, int32_t n_threads) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dq) return -1;
+    if (bwd_check(cu, n_seg, n_tokens, n_heads, head_dim, rows, n_rows)) return -1;
+    bwd_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.g = g; J.dout = dout;
+    J.n_tokens = n_tokens; J.n_heads = n_heads; J.head_dim = head_dim;
+    J.cu = cu; J.n_seg = n_seg; J.scale = scale;
+    J.rows = rows; J.n_rows = n_rows;
+    J.lse = lse; J.delta = delta; J.dq = dq; J.dg = g ? dg : NULL;
+    pthread_mutex_init(&J.lock, NULL);
+    run_threads(bwd_row_worker, &J, n_threads);
+    pthread_mutex_destroy(&J.lock);
+    return J.status;
+}
+
+/* Key-side pass: dk, dv [n_rows][H][D] for key rows; lse_all, delta_all [n_tokens][H] from the
+ * query-side pass over every token of the segments involved. */
+int h3o_attn_bwd_keys(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
+                      const uint16_t *dout, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                      const int64_t *cu, int32_t n_seg, double scale, const int64_t *rows, int64_t n_rows,
+                      const double *lse_all, const double *delta_all, double *dk, double *dv, int32_t n_threads) {
+    if (!q || !k || !v || !dout || !lse_all || !delta_all || !dk || !dv) return -1;
+    if (bwd_check(cu, n_seg, n_tokens, n_heads, head_dim, rows, n_rows)) return -1;
+    bwd_job J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.g = g; J.dout = dout;
+    J.n_tokens = n_tokens; J.n_heads = n_heads; J.head_dim = head_dim;
+    J.cu = cu; J.n_seg = n_seg; J.scale = scale;
+    J.rows = rows; J.n_rows = n_rows;
+    J.lse = (double *)lse_all; J.delta = (double *)delta_all; J.dk = dk; J.dv = dv;
+    pthread_mutex_init(&J.lock, NULL);
+    run_threads(bwd_key_worker, &J, n_threads);
+    pthread_mutex_destroy(&J.lock);
+    return J.status;
+}
+
 /* Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
 int h3o_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                   int64_t n_tokens, int32_t n_heads, int32_t head_dim,

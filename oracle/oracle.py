@@ -28,6 +28,8 @@ for a reader to check against the pages by eye:
                         backward reuses the forward's plan; Review and
                         validation: exact gradients).
 * ``attention_rows`` -- segment-masked softmax attention in fp64 (C, threads).
+* ``attention_backward`` -- its gradients (dq, dk, dv, dg) and log-sum-exp by
+                        the chain rule of softmax attention, in fp64 (C).
 * ``attention_dense`` -- the same result reached a second way: one dense
                         N x N logit matrix with -inf off the segment blocks.
 * ``adaln_rows``     -- per-segment AdaLN modulation / residual gating in fp64.
@@ -75,6 +77,13 @@ def _load():
         lib.h3o_attn_rows.argtypes = [ctypes.c_void_p] * 4 + [
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, i64p, ctypes.c_int32, ctypes.c_double,
             i64p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32]
+        bwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, i64p, ctypes.c_int32,
+                                            ctypes.c_double, i64p, ctypes.c_int64] + [ctypes.c_void_p] * 4 + [
+                                            ctypes.c_int32]
+        lib.h3o_attn_bwd_rows.restype = ctypes.c_int
+        lib.h3o_attn_bwd_rows.argtypes = bwd_args
+        lib.h3o_attn_bwd_keys.restype = ctypes.c_int
+        lib.h3o_attn_bwd_keys.argtypes = bwd_args
         lib.h3o_adaln_rows.restype = ctypes.c_int
         lib.h3o_adaln_rows.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 5 + [
             ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), i64p, i64p,
@@ -294,6 +303,72 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Optional[np.n
     return out
 
 
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Optional[np.ndarray], dout: np.ndarray,
+                       cu: Sequence[int], scale: float, q_rows: Optional[Sequence[int]] = None,
+                       k_rows: Optional[Sequence[int]] = None, threads: Optional[int] = None) -> dict:
+    """Gradients of ``attention_rows`` for the incoming output gradient ``dout``, fp64 (see h3_oracle.c).
+
+    The chain rule of softmax attention, term by term: for query rows, the
+    log-sum-exp ``lse``, ``delta`` = <do * sig(g), a> and the gradients
+    ``dq`` and ``dg`` (``dg`` only when ``g`` is given); for key rows, ``dk``
+    and ``dv``, which need ``lse`` and ``delta`` of every query of their
+    segment (computed here over those segments first).  Row lists default to
+    every token.  Returns a dict of fp64 arrays ``[rows, H, D]`` (``[rows, H]``
+    for ``lse`` and ``delta``).
+    """
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    g = None if g is None else _u16(g)
+    n, h, d = q.shape
+    for a in (k, v, dout) + ((g,) if g is not None else ()):
+        if a.shape != (n, h, d):
+            raise ValueError("q, k, v, g, dout must share one [N, H, D] shape")
+    cu = _i64(cu)
+    lib = _load()
+    nt = threads or default_threads()
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    gp = None if g is None else g.ctypes.data
+
+    def row_pass(rows):
+        rows = _i64(rows)
+        lse = np.empty((rows.shape[0], h), np.float64)
+        delta = np.empty((rows.shape[0], h), np.float64)
+        dq = np.empty((rows.shape[0], h, d), np.float64)
+        dg = np.empty((rows.shape[0], h, d), np.float64) if g is not None else None
+        rc = lib.h3o_attn_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, gp, dout.ctypes.data, n, h, d,
+                                   cu.ctypes.data_as(i64p), len(cu) - 1, float(scale), rows.ctypes.data_as(i64p),
+                                   rows.shape[0], lse.ctypes.data, delta.ctypes.data, dq.ctypes.data,
+                                   None if dg is None else dg.ctypes.data, nt)
+        if rc != 0:
+            raise ValueError(f"h3o_attn_bwd_rows failed with {rc}")
+        return lse, delta, dq, dg
+
+    out = {}
+    q_rows = np.arange(n) if q_rows is None else np.asarray(q_rows)
+    out["lse"], out["delta"], out["dq"], dg = row_pass(q_rows)
+    if dg is not None:
+        out["dg"] = dg
+    k_rows = np.arange(n) if k_rows is None else np.asarray(k_rows)
+    if len(k_rows):
+        # lse and delta of every query of the segments the key rows fall in
+        seg = np.searchsorted(cu, k_rows, side="right") - 1
+        need = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in np.unique(seg)])
+        lse_n, delta_n, _, _ = row_pass(need)
+        lse_all = np.zeros((n, h), np.float64)
+        delta_all = np.zeros((n, h), np.float64)
+        lse_all[need], delta_all[need] = lse_n, delta_n
+        kr = _i64(k_rows)
+        dk = np.empty((kr.shape[0], h, d), np.float64)
+        dv = np.empty((kr.shape[0], h, d), np.float64)
+        rc = lib.h3o_attn_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data, gp, dout.ctypes.data, n, h, d,
+                                   cu.ctypes.data_as(i64p), len(cu) - 1, float(scale), kr.ctypes.data_as(i64p),
+                                   kr.shape[0], lse_all.ctypes.data, delta_all.ctypes.data, dk.ctypes.data,
+                                   dv.ctypes.data, nt)
+        if rc != 0:
+            raise ValueError(f"h3o_attn_bwd_keys failed with {rc}")
+        out["dk"], out["dv"] = dk, dv
+    return out
+
+
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float64."""
     return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -379,6 +454,6 @@ def attention_flops(cu: Sequence[int], n_heads: int, head_dim: int) -> int:
 
 
 __all__ = ["build", "partition", "clip_segments", "seq2head", "head2seq", "seq2head_backward",
-           "head2seq_backward", "attention_rows",
+           "head2seq_backward", "attention_rows", "attention_backward",
            "attention_dense", "adaln_rows", "bf16_bits_to_f64", "EmptyPartition", "MODULATE",
            "GATE_RESIDUAL", "default_threads", "attention_flops"]

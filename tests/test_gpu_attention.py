@@ -90,6 +90,31 @@ def test_attention_drifting_logits(rise):
     compare(to_bits(o), oracle.attention_rows(qb, kb, vb, None, cu, SCALE), f"attn drifting {rise}")
 
 
+@pytest.mark.parametrize("lengths,qstd", [([1, 63, 64, 65], 1.0), ([300, 5, 700], 1.0), ([900, 130], 8.0)])
+def test_attention_lse_output(lengths, qstd):
+    """h3_packed_attn_lse: the same output bits as h3_packed_attn, plus the row
+    log-sum-exp.  The kernel's row sum adds the bf16-rounded probabilities its
+    PV step uses, so lse carries up to ~2^-9 relative error in the sum."""
+    cu = segment_offsets(lengths)
+    n, h = cu[-1], 3
+    say("attention lse", lengths, qstd)
+    q_bits = normal_bf16_bits((n, h, 128), seed=1400 + n, std=qstd)
+    bits = [q_bits] + [normal_bf16_bits((n, h, 128), seed=1401 + n + i) for i in range(3)]
+    q, k, v, g = (to_device(b) for b in bits)
+    o = torch.empty_like(q)
+    lse = torch.full((n, h), float("nan"), dtype=torch.float32, device="cuda")
+    _h3().packed_attn(q, k, v, g, o, cu, SCALE, lse=lse)
+    o2, _ = _run(q, k, v, g, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    ref = oracle.attention_backward(bits[0], bits[1], bits[2], bits[3], np.zeros_like(bits[0]), cu, SCALE,
+                                    k_rows=[])["lse"]
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    assert (err <= 4e-3 + 1e-6 * np.abs(ref)).all(), float(err.max())
+
+
 def test_attention_gate_zero_halves_exactly():
     cu = segment_offsets([200, 57])
     n, h = cu[-1], 2

@@ -378,6 +378,99 @@ def test_attention_row_subset_equals_full():
     assert np.array_equal(sub, full[rows])
 
 
+# ---- attention backward -----------------------------------------------------
+
+def _autograd_attention(q, k, v, g, dout, cu, scale):
+    """Dense N x N masked (gated) attention in float64 through torch autograd;
+    returns (lse, dq, dk, dv, dg) for the loss sum(dout * o)."""
+    f = lambda a: torch.from_numpy(oracle.bf16_bits_to_f64(a)).requires_grad_(True)  # noqa: E731
+    tq, tk, tv = f(q), f(k), f(v)
+    tg = None if g is None else f(g)
+    n = q.shape[0]
+    seg = np.searchsorted(np.asarray(cu), np.arange(n), side="right") - 1
+    same = torch.from_numpy(seg[:, None] == seg[None, :])
+    logits = torch.einsum("thd,uhd->htu", tq, tk) * scale
+    logits = logits.masked_fill(~same, float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)                       # [H, N]
+    o = torch.einsum("htu,uhd->thd", torch.softmax(logits, dim=-1), tv)
+    if tg is not None:
+        o = o * torch.sigmoid(tg)
+    (o * torch.from_numpy(oracle.bf16_bits_to_f64(dout))).sum().backward()
+    return (lse.T.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(),
+            None if tg is None else tg.grad.numpy())
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("qscale", [1.0, 8.0])
+def test_attention_backward_matches_library_autograd(gated, qscale):
+    cu = [0, 1, 37, 90, 130]
+    n, h, d = 130, 2, 16
+    q, k, v, g = _qkvg(n, h, d, seed=77, qscale=qscale)
+    dout = normal_bf16_bits((n, h, d), seed=81)
+    scale = 0.25
+    got = oracle.attention_backward(q, k, v, g if gated else None, dout, cu, scale)
+    lse, dq, dk, dv, dg = _autograd_attention(q, k, v, g if gated else None, dout, cu, scale)
+    np.testing.assert_allclose(got["lse"], lse, rtol=1e-12, atol=1e-12)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_allclose(got[name], ref, rtol=1e-9, atol=1e-10, err_msg=name)
+    if gated:
+        np.testing.assert_allclose(got["dg"], dg, rtol=1e-9, atol=1e-10)
+    else:
+        assert "dg" not in got
+
+
+def test_attention_backward_closed_forms():
+    n, h, d, scale = 40, 2, 8, 0.3
+    q, k, v, g = _qkvg(n, h, d, seed=90)
+    dout = normal_bf16_bits((n, h, d), seed=91)
+    # a one-token segment: p = 1, so ds = 0 -> dq = dk = 0, and dv = do * sig(g)
+    cu = [0, 1, 40]
+    r = oracle.attention_backward(q, k, v, g, dout, cu, scale, q_rows=[0], k_rows=[0])
+    sg = 1 / (1 + np.exp(-oracle.bf16_bits_to_f64(g[0])))
+    assert np.array_equal(r["dq"][0], np.zeros((h, d)))
+    assert np.array_equal(r["dk"][0], np.zeros((h, d)))
+    np.testing.assert_allclose(r["dv"][0], oracle.bf16_bits_to_f64(dout[0]) * sg, rtol=1e-15)
+    # identical keys in a segment: the softmax ignores q, so dq = 0
+    k2 = k.copy()
+    k2[1:40] = k[5]
+    r2 = oracle.attention_backward(q, k2, v, None, dout, cu, scale, q_rows=np.arange(1, 40), k_rows=[])
+    assert np.abs(r2["dq"]).max() < 1e-12
+    # g = 0: dg = do * a / 4 with a the ungated output
+    g0 = np.zeros_like(g)
+    r3 = oracle.attention_backward(q, k, v, g0, dout, cu, scale, k_rows=[])
+    a = oracle.attention_rows(q, k, v, None, cu, scale)
+    np.testing.assert_allclose(r3["dg"], oracle.bf16_bits_to_f64(dout) * a / 4, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_backward_segment_sums():
+    """Per segment and head: sum_u dk_u = 0 (the rows of ds sum to zero) and
+    sum_u dv_u = sum_t do_t * sig(g_t) (the rows of p sum to one)."""
+    cu = [0, 50, 51, 180]
+    n, h, d, scale = 180, 3, 8, 0.2
+    q, k, v, g = _qkvg(n, h, d, seed=95, qscale=2.0)
+    dout = normal_bf16_bits((n, h, d), seed=96)
+    r = oracle.attention_backward(q, k, v, g, dout, cu, scale)
+    e = oracle.bf16_bits_to_f64(dout) / (1 + np.exp(-oracle.bf16_bits_to_f64(g)))
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        np.testing.assert_allclose(r["dk"][a:b].sum(axis=0), 0.0, atol=1e-11)
+        np.testing.assert_allclose(r["dv"][a:b].sum(axis=0), e[a:b].sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_backward_row_subsets_equal_full():
+    cu = [0, 70, 100]
+    n, h, d = 100, 2, 8
+    q, k, v, g = _qkvg(n, h, d, seed=97)
+    dout = normal_bf16_bits((n, h, d), seed=98)
+    full = oracle.attention_backward(q, k, v, g, dout, cu, 0.3)
+    rows = [0, 69, 70, 99, 33]
+    part = oracle.attention_backward(q, k, v, g, dout, cu, 0.3, q_rows=rows, k_rows=rows[::-1])
+    for name in ("lse", "delta", "dq", "dg"):
+        assert np.array_equal(part[name], full[name][rows]), name
+    for name in ("dk", "dv"):
+        assert np.array_equal(part[name], full[name][rows[::-1]]), name
+
+
 def test_attention_flops_closed_form():
     w = WORKLOADS["128k_p4_qkvg"]
     assert oracle.attention_flops(w.cu, 14, 128) == 4 * 128 * 14 * (98304 ** 2 + 32768 ** 2)

@@ -491,9 +491,9 @@ h3_status h3_head2seq_backward(const h3_layout *L, const void *grad_dst, void *c
     return ok();
 }
 
-h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void *g, void *o, int64_t n_tokens,
-                         int32_t n_heads, int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale,
-                         void *stream, h3_plan_info *info) {
+static h3_status packed_attn_impl(const void *q, const void *k, const void *v, const void *g, void *o, float *lse,
+                                  int64_t n_tokens, int32_t n_heads, int32_t head_dim, const int64_t *cu,
+                                  int32_t n_segments, float scale, void *stream, h3_plan_info *info) {
     clear_info(info);
     if (!q || !k || !v || !o) return fail(H3_ERR_ARG, "q, k, v and o must be non-NULL");
     if (n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no tokens", (long long)n_tokens);
@@ -509,7 +509,9 @@ h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void
     const uint64_t bytes = (uint64_t)n_tokens * n_heads * head_dim * 2;
     std::vector<Range> ins{range_of(q, bytes, "q", 0), range_of(k, bytes, "k", 0), range_of(v, bytes, "v", 0)};
     if (g) ins.push_back(range_of(g, bytes, "g", 0));
-    if ((st = check_alias(ins, {range_of(o, bytes, "o", 0)})) != H3_OK) return st;
+    std::vector<Range> outs{range_of(o, bytes, "o", 0)};
+    if (lse) outs.push_back(range_of(lse, (uint64_t)n_tokens * n_heads * 4, "lse", 0));
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
 
     // work list: segments longest first, each expanded to heads x query tiles
     std::vector<int> order(n_segments);
@@ -518,7 +520,7 @@ h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void
                      [&](int x, int y) { return cu[x + 1] - cu[x] > cu[y + 1] - cu[y]; });
     h3::AttnArgs a;
     std::memset(&a, 0, sizeof a);
-    a.q = q; a.k = k; a.v = v; a.g = g; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.o = o; a.lse = lse;
     a.n_heads = (uint32_t)n_heads;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_entries = n_segments;
@@ -550,6 +552,22 @@ h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void
         info->tiles = total;
     }
     return ok();
+}
+
+h3_status h3_packed_attn(const void *q, const void *k, const void *v, const void *g, void *o, int64_t n_tokens,
+                         int32_t n_heads, int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale,
+                         void *stream, h3_plan_info *info) {
+    return packed_attn_impl(q, k, v, g, o, nullptr, n_tokens, n_heads, head_dim, cu, n_segments, scale, stream, info);
+}
+
+h3_status h3_packed_attn_lse(const void *q, const void *k, const void *v, const void *g, void *o, float *lse,
+                             int64_t n_tokens, int32_t n_heads, int32_t head_dim, const int64_t *cu,
+                             int32_t n_segments, float scale, void *stream, h3_plan_info *info) {
+    if (!lse) {
+        clear_info(info);
+        return fail(H3_ERR_ARG, "lse is NULL");
+    }
+    return packed_attn_impl(q, k, v, g, o, lse, n_tokens, n_heads, head_dim, cu, n_segments, scale, stream, info);
 }
 
 h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,

@@ -87,6 +87,7 @@ struct AttnArgs {
     const void *v;
     const void *g;          // may be null
     void *o;
+    float *lse;             // may be null: natural-log log-sum-exp of the scaled logits, [N][n_heads]
     uint32_t n_heads;       // heads in the buffers (row stride = n_heads * 128)
     float scale_log2;       // scale * log2(e)
     int32_t n_entries;

@@ -334,6 +334,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const float l_tot = half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (!q_valid) return;
+    if (a.lse && half == 0) {
+        // log-sum-exp of the scaled logits (natural log): the probabilities are
+        // 2^(c*s - m_run) / l_tot, so lse * log2(e) = m_run + log2(l_tot)
+        const float lse2 = m_run + __builtin_amdgcn_logf(l_tot);
+        a.lse[((uint64_t)a.seg_begin[lo] + (uint64_t)q_local) * a.n_heads + head] = lse2 * 0.6931471805599453f;
+    }
     uint16_t *op = static_cast<uint16_t *>(a.o) + base + (uint64_t)q_local * row_stride;
     const uint16_t *gp = a.g ? static_cast<const uint16_t *>(a.g) + base + (uint64_t)q_local * row_stride
                              : nullptr;

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3
 
 # names every build of libh3.so must export (the declarations of include/h3.h)
 EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
-           "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
+           "h3_packed_attn_lse", "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
            "h3_version")
 
 
@@ -83,12 +83,13 @@ def _load() -> ctypes.CDLL:
     lib.h3_seq2head_backward.argtypes = [lp, ctypes.POINTER(vp), vp, vp, ip]
     lib.h3_head2seq_backward.argtypes = [lp, vp, ctypes.POINTER(vp), vp, ip]
     lib.h3_packed_attn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
+    lib.h3_packed_attn_lse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_adaln_segment.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, i64p, i32, f32, vp, ip]
     lib.h3_partition.argtypes = [i64, i32, i32, i64p, i64p]
     lib.h3_clip_segments.argtypes = [i64p, i32, i64, i64, ctypes.POINTER(i32), i64p, i64p]
     lib.h3_clip_segments.restype = i32
     for name in ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward",
-                 "h3_packed_attn", "h3_adaln_segment", "h3_partition"):
+                 "h3_packed_attn", "h3_packed_attn_lse", "h3_adaln_segment", "h3_partition"):
         getattr(lib, name).restype = ctypes.c_int
     lib.h3_status_string.argtypes = [ctypes.c_int]
     lib.h3_status_string.restype = ctypes.c_char_p
@@ -164,19 +165,27 @@ def _stream_ptr(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev_bf16(t, name: str, shape: Optional[Tuple[int, ...]] = None) -> int:
+def _dev_tensor(t, name: str, dtype, shape: Optional[Tuple[int, ...]] = None) -> int:
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU, got {t.device}")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
+
+
+def _dev_bf16(t, name: str, shape: Optional[Tuple[int, ...]] = None) -> int:
+    return _dev_tensor(t, name, _torch().bfloat16, shape)
+
+
+def _dev_f32(t, name: str, shape: Optional[Tuple[int, ...]] = None) -> int:
+    return _dev_tensor(t, name, _torch().float32, shape)
 
 
 def head_split(n_heads: int, world: int) -> List[Tuple[int, int]]:
@@ -262,8 +271,12 @@ def head2seq_backward(grad_dst, grad_src: Sequence, world: int, rank: int = -1, 
     return _info(info)
 
 
-def packed_attn(q, k, v, g, o, cu_seqlens: Sequence[int], scale: float, stream=None) -> PlanInfo:
-    """Segment-masked attention of [N, H, 128] operands; ``g`` may be None."""
+def packed_attn(q, k, v, g, o, cu_seqlens: Sequence[int], scale: float, stream=None, lse=None) -> PlanInfo:
+    """Segment-masked attention of [N, H, 128] operands; ``g`` may be None.
+
+    With ``lse`` (a float32 [N, H] device tensor) the call also writes the
+    per-row log-sum-exp of the scaled logits (``h3_packed_attn_lse``).
+    """
     n, h, d = q.shape
     shp = (n, h, d)
     ptrs = [_dev_bf16(t, nm, shp) for t, nm in ((q, "q"), (k, "k"), (v, "v"))]
@@ -271,8 +284,13 @@ def packed_attn(q, k, v, g, o, cu_seqlens: Sequence[int], scale: float, stream=N
     op = _dev_bf16(o, "o", shp)
     cu = _i64_array(cu_seqlens)
     info = _PlanInfo()
-    _check(_lib.h3_packed_attn(ptrs[0], ptrs[1], ptrs[2], gp, op, n, h, d, cu, len(cu_seqlens) - 1,
-                               float(scale), _stream_ptr(stream), ctypes.byref(info)))
+    if lse is None:
+        _check(_lib.h3_packed_attn(ptrs[0], ptrs[1], ptrs[2], gp, op, n, h, d, cu, len(cu_seqlens) - 1,
+                                   float(scale), _stream_ptr(stream), ctypes.byref(info)))
+    else:
+        lp = _dev_f32(lse, "lse", (n, h))
+        _check(_lib.h3_packed_attn_lse(ptrs[0], ptrs[1], ptrs[2], gp, op, lp, n, h, d, cu, len(cu_seqlens) - 1,
+                                       float(scale), _stream_ptr(stream), ctypes.byref(info)))
     return _info(info)
 
 
