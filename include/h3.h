@@ -199,6 +199,38 @@ h3_status h3_packed_attn_lse(const void *q, const void *k, const void *v, const 
                              void *stream, h3_plan_info *info);
 
 /* ------------------------------------------------------------------------
+ * h3_packed_attn_backward -- gradients of h3_packed_attn for the backward
+ * pass (the forward's passages; the chain rule of softmax attention with the
+ * optional sigmoid gate).  With p = softmax over the query's own segment of
+ * scale*<q,k>, a = sum p v, o = a * sig(g) and the incoming gradient do:
+ *   e   = do * sig(g)                      dg = do * o * (1 - sig(g))
+ *   D   = <do, o>  (= <e, a>)              ds = p * (<e, v> - D)
+ *   dq  = scale * sum_u ds k_u             dk = scale * sum_t ds q_t
+ *   dv  = sum_t p e_t
+ * (sig = 1 and no dg when g is NULL).  Cross-segment blocks are skipped as in
+ * the forward.
+ *
+ * q, k, v, g, o, dout: device, bf16 [N][H][128]; o is the forward output.
+ * lse: device, fp32 [N][H], from h3_packed_attn_lse of the same inputs.
+ * dq, dk, dv: device, bf16 [N][H][128], written for every token.
+ * dg: device, bf16 [N][H][128]; required iff g != NULL.
+ * workspace: device scratch of at least h3_packed_attn_backward_workspace()
+ *      bytes, owned by the caller (the library allocates nothing); its
+ *      contents on entry do not matter and on return are unspecified.
+ * Outputs must not overlap inputs, the workspace or each other.
+ * Launches: 3 (row terms e, D, dg; then dk/dv; then dq).
+ * ------------------------------------------------------------------------ */
+int64_t h3_packed_attn_backward_workspace(int64_t n_tokens, int32_t n_heads, int32_t gated);
+
+h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, const void *g,
+                                  const void *o, const void *dout, const float *lse,
+                                  void *dq, void *dk, void *dv, void *dg,
+                                  void *workspace, int64_t workspace_bytes,
+                                  int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                  const int64_t *cu_seqlens, int32_t n_segments, float scale,
+                                  void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
  * h3_adaln_segment -- per-segment AdaLN on one rank's token interval.
  *
  * [DIST] Partition Contract: segment boundaries are clipped to the rank's

@@ -210,6 +210,7 @@ static void bwd_row_one(const bwd_job *J, int64_t r, int32_t h, double *z, doubl
     }
     J->lse[r * H + h] = lse;
     J->delta[r * H + h] = delta;
+    if (!J->dq) return;     /* only lse and delta asked for */
     /* dq_t = scale * sum_u p_tu (<e_t, v_u> - D_t) k_u */
     double *dq = J->dq + (r * H + h) * D;
     for (int32_t d = 0; d < D; ++d) dq[d] = 0.0;
@@ -312,12 +313,13 @@ static int bwd_check(const int64_t *cu, int32_t n_seg, int64_t n_tokens, int32_t
     return 0;
 }
 
-/* Query-side pass: lse, delta [n_rows][H]; dq, dg [n_rows][H][D] (dg NULL when g is NULL). */
+/* Query-side pass: lse, delta [n_rows][H]; dq, dg [n_rows][H][D] (dg NULL when g is NULL; dq NULL
+ * when only lse and delta are wanted). */
 int h3o_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *dout, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                       const int64_t *cu, int32_t n_seg, double scale, const int64_t *rows, int64_t n_rows,
                       double *lse, double *delta, double *dq, double *dg, int32_t n_threads) {
-    if (!q || !k || !v || !dout || !lse || !delta || !dq) return -1;
+    if (!q || !k || !v || !dout || !lse || !delta) return -1;
     if (bwd_check(cu, n_seg, n_tokens, n_heads, head_dim, rows, n_rows)) return -1;
     bwd_job J;
     memset(&J, 0, sizeof J);

@@ -328,16 +328,16 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Optional[
     i64p = ctypes.POINTER(ctypes.c_int64)
     gp = None if g is None else g.ctypes.data
 
-    def row_pass(rows):
+    def row_pass(rows, gradients=True):
         rows = _i64(rows)
         lse = np.empty((rows.shape[0], h), np.float64)
         delta = np.empty((rows.shape[0], h), np.float64)
-        dq = np.empty((rows.shape[0], h, d), np.float64)
-        dg = np.empty((rows.shape[0], h, d), np.float64) if g is not None else None
+        dq = np.empty((rows.shape[0], h, d), np.float64) if gradients else None
+        dg = np.empty((rows.shape[0], h, d), np.float64) if g is not None and gradients else None
         rc = lib.h3o_attn_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, gp, dout.ctypes.data, n, h, d,
                                    cu.ctypes.data_as(i64p), len(cu) - 1, float(scale), rows.ctypes.data_as(i64p),
-                                   rows.shape[0], lse.ctypes.data, delta.ctypes.data, dq.ctypes.data,
-                                   None if dg is None else dg.ctypes.data, nt)
+                                   rows.shape[0], lse.ctypes.data, delta.ctypes.data,
+                                   None if dq is None else dq.ctypes.data, None if dg is None else dg.ctypes.data, nt)
         if rc != 0:
             raise ValueError(f"h3o_attn_bwd_rows failed with {rc}")
         return lse, delta, dq, dg
@@ -352,10 +352,15 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Optional[
         # lse and delta of every query of the segments the key rows fall in
         seg = np.searchsorted(cu, k_rows, side="right") - 1
         need = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in np.unique(seg)])
-        lse_n, delta_n, _, _ = row_pass(need)
         lse_all = np.zeros((n, h), np.float64)
         delta_all = np.zeros((n, h), np.float64)
-        lse_all[need], delta_all[need] = lse_n, delta_n
+        have = np.zeros(n, bool)
+        have[q_rows] = True
+        if have[need].all():            # the query-side pass above already covers them
+            lse_all[q_rows], delta_all[q_rows] = out["lse"], out["delta"]
+        else:
+            lse_n, delta_n, _, _ = row_pass(need, gradients=False)
+            lse_all[need], delta_all[need] = lse_n, delta_n
         kr = _i64(k_rows)
         dk = np.empty((kr.shape[0], h, d), np.float64)
         dv = np.empty((kr.shape[0], h, d), np.float64)

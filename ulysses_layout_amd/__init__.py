@@ -7,6 +7,6 @@ fails if the library has not been built.
 """
 from .h3 import (  # noqa: F401
     EXPORTS, H3_ADALN_GATE_RESIDUAL, H3_ADALN_MODULATE, HEAD_DIM, H3Error, Layout, PlanInfo,
-    adaln_segment, clip_segments, head2seq, head2seq_backward, head_split, library, packed_attn, partition,
-    seq2head, seq2head_backward, version,
+    adaln_segment, clip_segments, head2seq, head2seq_backward, head_split, library, packed_attn,
+    packed_attn_backward, packed_attn_backward_workspace, partition, seq2head, seq2head_backward, version,
 )

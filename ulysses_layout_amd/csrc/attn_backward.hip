@@ -1,0 +1,595 @@
+// attn_backward.hip -- gradients of the segment-masked packed attention
+// (packed_attn.hip) and of its sigmoid gate, for the backward pass.
+//
+// The forward's passages ("Distributed H3 Execution", introduction: attention
+// over the native packed sequence; "[perf] Harden Ulysses agreement and tune
+// bounded H3 transfers", Problem and behavior: QKV/QKVG operands) define the
+// function; its gradient is the chain rule of softmax attention.  With
+// p_tu = exp(scale*<q_t,k_u> - lse_t) over the keys of t's segment,
+// a_t = sum_u p_tu v_u, o_t = a_t * sig(g_t) and the incoming gradient do_t:
+//   e_t = do_t * sig(g_t),  dg_t = do_t * o_t * (1 - sig(g_t)),  D_t = <do_t, o_t>,
+//   ds_tu = p_tu (<e_t, v_u> - D_t),
+//   dq_t = scale sum_u ds_tu k_u,  dk_u = scale sum_t ds_tu q_t,  dv_u = sum_t p_tu e_t.
+//
+// Three launches:
+//   k_attn_bwd_pre   one 16-lane group per (token, head) row: e, dg and D.
+//   k_attn_bwd_dkdv  one workgroup per (segment, head, 128-key block).  The
+//                    block's K and V stay in LDS; 64-query tiles of Q and e
+//                    stream through LDS (buffer loads to LDS, double
+//                    buffered).  Waves 0-3 own dK and waves 4-7 own dV of the
+//                    32-key block w%4, so each holds one 64-register
+//                    accumulator (both would not fit beside the tiles' working
+//                    set); S is formed by both waves of a block.  Per 32-query
+//                    half of a tile, with the keys as MFMA columns (lane =
+//                    key): S = Q K^T and P from it with lse read per row from
+//                    LDS; the dV wave adds e^T P, the dK wave forms dP = e V^T
+//                    and dS = P (dP - D) and adds Q^T dS, the transposing LDS
+//                    load supplying e^T and Q^T.
+//   k_attn_bwd_dq    the forward's structure with the roles of the operands
+//                    reassigned: one workgroup per (segment, head, 256-query
+//                    tile), lane = query.  Per 64-key tile: S^T = K Q^T and
+//                    dP^T = V e^T (Q and e rows in registers), dS^T from them
+//                    with the lane's own lse and D, dQ^T += K^T dS^T (K^T
+//                    through the transposing LDS load).
+// Rows past a segment's end are clamped to its last row on load; keys there
+// are masked to -inf (dq kernel), queries there get lse = +inf so their p is 0
+// (dk/dv kernel), and no output row past the end is written.
+//
+// MFMA layouts (v_mfma_f32_32x32x16_bf16), LDS swizzle and the transposing
+// read follow packed_attn.hip; see the comments there.
+#include "h3_internal.h"
+
+namespace h3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kD = H3_HEAD_DIM;          // 128
+constexpr int kBN = 64;                  // keys per tile (dq) / queries per tile (dk/dv)
+constexpr int kTileElems = kBN * kD;
+constexpr int kWaves = kBwdThreads / 64; // 8
+constexpr int kLoadsPerTile = kBN / (4 * kWaves);          // 16-byte loads per lane per 64-row tile
+constexpr int kLoadsPerKBlock = kBwdKBlock / (4 * kWaves); // per 128-row key block
+constexpr int kBufferWord3 = 0x00020000;
+constexpr float kLog2e = 1.4426950408889634f;
+static_assert(kBwdQBlock == 32 * kWaves, "one 32-query block per wave");
+static_assert(kBwdKBlock == 32 * (kWaves / 2), "a dK wave and a dV wave per 32-key block");
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
+
+// 16-byte chunk c of tile row r sits at chunk c ^ f(r) (as in packed_attn.hip)
+__device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r)) << 3); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_void *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 lds_b128(const uint16_t *p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+
+// offsets of the transposing reads that give the A operand X^T (32 channels x
+// 16 rows) of a 16-row step from a row-major tile X: k slot (half, jj) of the
+// step is tile row 8*(jj/4) + 4*half + jj%4, as the C layout orders rows
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[kD / 32][2]) {
+    const int half = lane >> 5, grp = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int r = 8 * s2 + 4 * half + (i >> 2);
+            const int col = db * 32 + 16 * (grp & 1) + 4 * (i & 3);
+            off[db][s2] = swz(r, col >> 3) + (col & 7);
+        }
+}
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile_rows, const int (&off)[kD / 32][2], int db) {
+    const bf16x4 a = lds_read_tr(tile_rows + off[db][0]);
+    const bf16x4 b = lds_read_tr(tile_rows + off[db][1]);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The same offsets in closed form, from three per-lane values, for kernels short of registers:
+//   swz(l32, 2ks + half)  = rb + ((ks ^ rx) << 4)
+//   tr offset (db, s2)    = tb[s2] + ((db ^ tx) << 5)
+struct CompactOffsets {
+    int rb, rx, tb0, tb1, tx;
+};
+__device__ __forceinline__ CompactOffsets compact_offsets(int lane) {
+    const int l32 = lane & 31, half = lane >> 5, grp = lane >> 4, i = lane & 15;
+    const int f = swz_f(l32);
+    CompactOffsets c;
+    c.rb = l32 * kD + 8 * (half ^ (f & 1));
+    c.rx = f >> 1;
+    const int c0 = 2 * (grp & 1) + ((i & 3) >> 1);
+    c.tb0 = (4 * half + (i >> 2)) * kD + 8 * (c0 ^ half) + 4 * (i & 1);
+    c.tb1 = (8 + 4 * half + (i >> 2)) * kD + 8 * (c0 ^ (2 + half)) + 4 * (i & 1);
+    c.tx = i >> 2;
+    return c;
+}
+// Expand inside a tile's work; the empty asm keeps the expansion from being hoisted out of the
+// loop (where every (LDS object, offset) address would stay live across it).
+__device__ __forceinline__ void expand_offsets(CompactOffsets c, int (&ro)[kD / 16], int (&to)[kD / 32][2]) {
+    asm volatile("" : "+v"(c.rb), "+v"(c.rx), "+v"(c.tb0), "+v"(c.tb1), "+v"(c.tx));
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) ro[ks] = c.rb + ((ks ^ c.rx) << 4);
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+        to[db][0] = c.tb0 + ((db ^ c.tx) << 5);
+        to[db][1] = c.tb1 + ((db ^ c.tx) << 5);
+    }
+}
+
+// which (entry, local index) a workgroup id belongs to in a longest-first work list
+__device__ __forceinline__ int find_entry(const AttnBwdArgs &a, int w) {
+    int lo = 0, hi = a.n_entries - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.wg_prefix[mid] <= w) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// row terms: e = do * sig(g), dg = do * o * (1 - sig(g)), D = <do, o>
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attn_bwd_pre(AttnBwdArgs a) {
+    const uint32_t row = blockIdx.x * kBwdPreRowsPerWg + (threadIdx.x >> 4);
+    if (row >= a.n_rows) return;
+    const uint64_t off = (uint64_t)row * (kD / 8) + (threadIdx.x & 15);
+    const u32x4 dov = __builtin_nontemporal_load(static_cast<const u32x4 *>(a.dout) + off);
+    const u32x4 ov = __builtin_nontemporal_load(static_cast<const u32x4 *>(a.o) + off);
+    float dsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dsum += bf16_lo(dov[w]) * bf16_lo(ov[w]) + bf16_hi(dov[w]) * bf16_hi(ov[w]);
+    if (a.g) {
+        const u32x4 gv = __builtin_nontemporal_load(static_cast<const u32x4 *>(a.g) + off);
+        u32x4 ev, dgv;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float s0 = sigmoid(bf16_lo(gv[w])), s1 = sigmoid(bf16_hi(gv[w]));
+            ev[w] = pack_bf16x2(bf16_lo(dov[w]) * s0, bf16_hi(dov[w]) * s1);
+            dgv[w] = pack_bf16x2(bf16_lo(dov[w]) * bf16_lo(ov[w]) * (1.0f - s0),
+                                 bf16_hi(dov[w]) * bf16_hi(ov[w]) * (1.0f - s1));
+        }
+        static_cast<u32x4 *>(a.e)[off] = ev;
+        __builtin_nontemporal_store(dgv, static_cast<u32x4 *>(a.dg) + off);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 16);
+    if ((threadIdx.x & 15) == 0) a.delta[row] = dsum;
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: one workgroup per (segment, head, 128-key block)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a) {
+    // distinct LDS objects, so loads into one buffer never look like they alias reads of another
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kBwdKBlock * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kBwdKBlock * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sE0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sE1[kTileElems];
+    __shared__ __attribute__((aligned(16))) float sL0[kBN];
+    __shared__ __attribute__((aligned(16))) float sL1[kBN];
+    __shared__ __attribute__((aligned(16))) float sD0[kBN];
+    __shared__ __attribute__((aligned(16))) float sD1[kBN];
+
+    const int lo = find_entry(a, blockIdx.x);
+    const int seg_len = a.seg_len[lo];
+    const int kblocks = (seg_len + kBwdKBlock - 1) / kBwdKBlock;
+    const int local = blockIdx.x - a.wg_prefix[lo];
+    const int head = local / kblocks;
+    const int key0 = (local - head * kblocks) * kBwdKBlock;          // segment-relative first key
+    const uint64_t row_stride = (uint64_t)a.n_heads * kD;
+    const uint64_t seg_row0 = (uint64_t)a.seg_begin[lo];
+    const uint64_t base = seg_row0 * row_stride + (uint64_t)head * kD;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int kb = wave & 3;             // key block of this wave: keys key0 + 32*kb ..
+    const bool dv_wave = (wave >> 2) != 0;   // waves 0-3 accumulate dK, waves 4-7 dV
+    const int row_bytes = (int)(row_stride * 2);
+
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base;
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
+    const uint16_t *ep = static_cast<const uint16_t *>(a.e) + base;
+
+    // LDS rows loaded by this lane: 4*(kWaves*i + wave) + lane/16, chunk (lane%16) ^ f(row)
+    const int ld_row0 = 4 * wave + (lane >> 4);
+    const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
+
+    // ---- the block's keys and values, once -------------------------------------------
+    {
+        const uint64_t blk0 = (uint64_t)key0 * row_stride;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kp + blk0), 0, kBwdKBlock * row_bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vp + blk0), 0, kBwdKBlock * row_bytes, kBufferWord3);
+        const int last = seg_len - 1 - key0;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerKBlock; ++i) {
+            int key = ld_row0 + 4 * kWaves * i;
+            key = key < last ? key : last;
+            const int off = key * row_bytes + ld_chunk * 16;
+            const int lds_row = 4 * (kWaves * i + wave);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + lds_row * kD), 16, off, 0, 0, 0);
+        }
+    }
+    const int n_qt = (seg_len + kBN - 1) / kBN;
+    int ld_off[kLoadsPerTile];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) ld_off[i] = (ld_row0 + 4 * kWaves * i) * row_bytes + ld_chunk * 16;
+    auto issue_tile = [&](int qt, uint16_t *dq_, uint16_t *de_) {
+        const uint64_t tile0 = (uint64_t)qt * kBN * row_stride;
+        const __amdgpu_buffer_rsrc_t rq =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(qp + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t re =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(ep + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const int last = seg_len - 1 - qt * kBN;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerTile; ++i) {
+            int off = ld_off[i];
+            if ((qt + 1) * kBN > seg_len) {
+                int row = ld_row0 + 4 * kWaves * i;
+                row = row < last ? row : last;
+                off = row * row_bytes + ld_chunk * 16;
+            }
+            const int lds_row = 4 * (kWaves * i + wave);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dq_ + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + lds_row * kD), 16, off, 0, 0, 0);
+        }
+    };
+    // lse (base 2, +inf past the segment end) and D of a query tile: wave 0 and wave 1, one value per lane
+    auto row_value = [&](int qt) -> float {
+        const int qrow = qt * kBN + lane;
+        if (wave == 0) {
+            return qrow < seg_len ? a.lse[(seg_row0 + qrow) * a.n_heads + head] * kLog2e : __builtin_inff();
+        }
+        return qrow < seg_len ? a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
+    };
+
+    // per-lane LDS offsets: row l32 of a 32-row block, chunk 2ks+half (f(row) repeats every 16 rows,
+    // so the same offsets serve the query half qsel*32 of a tile and the key block kb*32)
+    const CompactOffsets coff = compact_offsets(lane);
+    const int k_base = __builtin_amdgcn_readfirstlane(kb * 32 * kD);     // this wave's key block
+
+    f32x16 acc[kD / 32];         // dK^T or dV^T of the wave's 32 keys: lane = key, registers = channels
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
+
+    auto compute_tile = [&](const uint16_t *tq, const uint16_t *te, const float *tl, const float *td) {
+        // The LDS objects span more than the 64 KB a read's immediate offset reaches, so every
+        // (object, offset) pair needs its own address register: the offsets are expanded here,
+        // per tile, rather than kept live across the loop.
+        int ro[kD / 16], to[kD / 32][2];
+        expand_offsets(coff, ro, to);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {                 // the two 32-query halves of the tile
+            const int q_base = qh * 32 * kD;
+            // S = Q K^T, 32 queries x 32 keys, lane = key
+            f32x16 s = {};
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + q_base + ro[ks]),
+                                                            lds_b128(sK + k_base + ro[ks]), s, 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (dv_wave) {
+                // P (register r holds query row qh*32 + 8*(r/4) + 4*half + r%4), then dV^T += e^T P
+                uint32_t pw[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
+                    float p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i + e], a.scale_log2, -lv[e]));
+                    pw[2 * i] = pack_bf16x2(p[0], p[1]);
+                    pw[2 * i + 1] = pack_bf16x2(p[2], p[3]);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {       // 16-query step j uses registers 8j..8j+7
+                    const bf16x8 pb =
+                        __builtin_bit_cast(bf16x8, (u32x4){pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
+#pragma unroll
+                    for (int db = 0; db < kD / 32; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_frag(te + q_base + 16 * j * kD, to, db), pb, acc[db], 0, 0, 0);
+                }
+            } else {
+                // dP = e V^T, dS = P (dP - D), then dK^T += Q^T dS
+                f32x16 dp = {};
+#pragma unroll
+                for (int ks = 0; ks < kD / 16; ++ks)
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + q_base + ro[ks]),
+                                                                 lds_b128(sV + k_base + ro[ks]), dp, 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+                uint32_t dw[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
+                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
+                    float ds[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i + e], a.scale_log2, -lv[e])) *
+                                (dp[4 * i + e] - dv[e]);
+                    dw[2 * i] = pack_bf16x2(ds[0], ds[1]);
+                    dw[2 * i + 1] = pack_bf16x2(ds[2], ds[3]);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16x8 dsb =
+                        __builtin_bit_cast(bf16x8, (u32x4){dw[4 * j], dw[4 * j + 1], dw[4 * j + 2], dw[4 * j + 3]});
+#pragma unroll
+                    for (int db = 0; db < kD / 32; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_frag(tq + q_base + 16 * j * kD, to, db), dsb, acc[db], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // ---- prologue: tile 0 -----------------------------------------------------------
+    issue_tile(0, sQ0, sE0);
+    if (wave < 2) {
+        const float rv = row_value(0);
+        (wave == 0 ? sL0 : sD0)[lane] = rv;
+    }
+    // ---- main loop over query tiles, two per trip so buffer addresses are constants -
+    for (int qt = 0; qt < n_qt; qt += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): this lane's loads of tile qt landed
+        __syncthreads();
+        float nv = 0.f;
+        if (qt + 1 < n_qt) {
+            issue_tile(qt + 1, sQ1, sE1);
+            if (wave < 2) nv = row_value(qt + 1);
+        }
+        compute_tile(sQ0, sE0, sL0, sD0);
+        if (qt + 1 < n_qt && wave < 2) (wave == 0 ? sL1 : sD1)[lane] = nv;
+        if (qt + 1 >= n_qt) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (qt + 2 < n_qt) {
+            issue_tile(qt + 2, sQ0, sE0);
+            if (wave < 2) nv = row_value(qt + 2);
+        }
+        compute_tile(sQ1, sE1, sL1, sD1);
+        if (qt + 2 < n_qt && wave < 2) (wave == 0 ? sL0 : sD0)[lane] = nv;
+    }
+
+    // ---- store this wave's 32 keys: lane = key, register r = channel db*32 + 8*(r/4) + 4*half + r%4
+    const int key = key0 + kb * 32 + l32;             // segment-relative key of this lane
+    if (key >= seg_len) return;
+    uint16_t *outp = static_cast<uint16_t *>(dv_wave ? a.dv : a.dk) + base + (uint64_t)key * row_stride;
+    const float mul = dv_wave ? 1.0f : a.scale;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+            const int d0 = db * 32 + 8 * (r / 4) + 4 * half;      // 4 consecutive channels
+            const u32x2 w = {pack_bf16x2(acc[db][r] * mul, acc[db][r + 1] * mul),
+                             pack_bf16x2(acc[db][r + 2] * mul, acc[db][r + 3] * mul)};
+            *reinterpret_cast<u32x2 *>(outp + d0) = w;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dq: one workgroup per (segment, head, 256-query tile), lane = query
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kTileElems];
+
+    const int lo = find_entry(a, blockIdx.x);
+    const int seg_len = a.seg_len[lo];
+    const int tiles = (seg_len + kBwdQBlock - 1) / kBwdQBlock;
+    const int local = blockIdx.x - a.wg_prefix[lo];
+    const int head = local / tiles;
+    const int qtile = local - head * tiles;
+    const uint64_t row_stride = (uint64_t)a.n_heads * kD;
+    const uint64_t seg_row0 = (uint64_t)a.seg_begin[lo];
+    const uint64_t base = seg_row0 * row_stride + (uint64_t)head * kD;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int q_local = qtile * kBwdQBlock + wave * 32 + l32;
+    const bool q_valid = q_local < seg_len;
+    const int row_bytes = (int)(row_stride * 2);
+
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
+
+    // this lane's q and e rows as B operands (k slots: 8 channels of chunk 2ks+half)
+    bf16x8 qreg[kD / 16], ereg[kD / 16];
+    {
+        const uint64_t r = (uint64_t)(q_valid ? q_local : 0) * row_stride;
+        const u32x4 *qs = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + base + r);
+        const u32x4 *es = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.e) + base + r);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+            u32x4 x = qs[ks * 2 + half], y = es[ks * 2 + half];
+            if (!q_valid) {
+                x = (u32x4){0u, 0u, 0u, 0u};
+                y = (u32x4){0u, 0u, 0u, 0u};
+            }
+            qreg[ks] = __builtin_bit_cast(bf16x8, x);
+            ereg[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+    const uint64_t lrow = (seg_row0 + (uint64_t)(q_valid ? q_local : 0)) * a.n_heads + head;
+    const float lse2 = a.lse[lrow] * kLog2e;
+    const float delta = a.delta[lrow];
+
+    const CompactOffsets coff = compact_offsets(lane);
+
+    const int ld_row0 = 4 * wave + (lane >> 4);
+    const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
+    const int n_kt = (seg_len + kBN - 1) / kBN;
+    int ld_off[kLoadsPerTile];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) ld_off[i] = (ld_row0 + 4 * kWaves * i) * row_bytes + ld_chunk * 16;
+    auto issue_tile = [&](int kt, uint16_t *dk_, uint16_t *dv_) {
+        const uint64_t tile0 = (uint64_t)kt * kBN * row_stride;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kp + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vp + tile0), 0, kBN * row_bytes, kBufferWord3);
+        const int last = seg_len - 1 - kt * kBN;
+#pragma unroll
+        for (int i = 0; i < kLoadsPerTile; ++i) {
+            int off = ld_off[i];
+            if ((kt + 1) * kBN > seg_len) {
+                int key = ld_row0 + 4 * kWaves * i;
+                key = key < last ? key : last;
+                off = key * row_bytes + ld_chunk * 16;
+            }
+            const int lds_row = 4 * (kWaves * i + wave);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk_ + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv_ + lds_row * kD), 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
+
+    auto compute_tile = [&](int kt, const uint16_t *tk, const uint16_t *tv) {
+        int k_off[kD / 16], t_off[kD / 32][2];
+        expand_offsets(coff, k_off, t_off);
+        // one 32-key block at a time: S^T = K Q^T and dP^T = V e^T (lane = query), then
+        // dS^T = P^T (dP^T - D) packed as the B operand of two 16-key steps, then dQ^T += K^T dS^T
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tk + kb * 32 * kD + k_off[ks]), qreg[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tv + kb * 32 * kD + k_off[ks]), ereg[ks], dp, 0, 0,
+                                                             0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if ((kt + 1) * kBN > seg_len) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * kBN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= seg_len) s[r] = -__builtin_inff();
+                }
+            }
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 8 * j + 2 * e;
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -lse2));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, -lse2));
+                    w4[e] = pack_bf16x2(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+                }
+                dsb[j] = __builtin_bit_cast(bf16x8, (u32x4){w4[0], w4[1], w4[2], w4[3]});
+            }
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_frag(tk + (kb * 32 + 16 * j) * kD, t_off, db), dsb[j], acc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        }
+    };
+
+    issue_tile(0, sK0, sV0);
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (kt + 1 < n_kt) issue_tile(kt + 1, sK1, sV1);
+        compute_tile(kt, sK0, sV0);
+        if (kt + 1 >= n_kt) break;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (kt + 2 < n_kt) issue_tile(kt + 2, sK0, sV0);
+        compute_tile(kt + 1, sK1, sV1);
+    }
+
+    if (!q_valid) return;
+    uint16_t *dqp = static_cast<uint16_t *>(a.dq) + base + (uint64_t)q_local * row_stride;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            const int d0 = db * 32 + 8 * grp + 4 * half;
+            const u32x2 w = {pack_bf16x2(acc[db][grp * 4] * a.scale, acc[db][grp * 4 + 1] * a.scale),
+                             pack_bf16x2(acc[db][grp * 4 + 2] * a.scale, acc[db][grp * 4 + 3] * a.scale)};
+            *reinterpret_cast<u32x2 *>(dqp + d0) = w;
+        }
+}
+
+hipError_t launch_attn_bwd_pre(const AttnBwdArgs &a, hipStream_t s, int *grid_x) {
+    const uint32_t gx = (a.n_rows + kBwdPreRowsPerWg - 1) / kBwdPreRowsPerWg;
+    if (grid_x) *grid_x = (int)gx;
+    if (gx == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_attn_bwd_pre, dim3(gx), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv(const AttnBwdArgs &a, int n_workgroups, hipStream_t s) {
+    if (n_workgroups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_attn_bwd_dkdv, dim3(n_workgroups), dim3(kBwdThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs &a, int n_workgroups, hipStream_t s) {
+    if (n_workgroups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_attn_bwd_dq, dim3(n_workgroups), dim3(kBwdThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace h3

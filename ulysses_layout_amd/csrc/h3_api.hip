@@ -570,6 +570,106 @@ h3_status h3_packed_attn_lse(const void *q, const void *k, const void *v, const 
     return packed_attn_impl(q, k, v, g, o, lse, n_tokens, n_heads, head_dim, cu, n_segments, scale, stream, info);
 }
 
+static int64_t bwd_delta_bytes(int64_t rows) { return ((rows * 4 + 255) / 256) * 256; }
+
+int64_t h3_packed_attn_backward_workspace(int64_t n_tokens, int32_t n_heads, int32_t gated) {
+    if (n_tokens < 1 || n_heads < 1) return 0;
+    const int64_t rows = n_tokens * n_heads;
+    return bwd_delta_bytes(rows) + (gated ? rows * H3_HEAD_DIM * 2 : 0);
+}
+
+h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, const void *g, const void *o,
+                                  const void *dout, const float *lse, void *dq, void *dk, void *dv, void *dg,
+                                  void *workspace, int64_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
+                                  int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale, void *stream,
+                                  h3_plan_info *info) {
+    clear_info(info);
+    if (!q || !k || !v || !o || !dout || !lse) return fail(H3_ERR_ARG, "q, k, v, o, dout and lse must be non-NULL");
+    if (!dq || !dk || !dv) return fail(H3_ERR_ARG, "dq, dk and dv must be non-NULL");
+    if ((g == nullptr) != (dg == nullptr)) return fail(H3_ERR_ARG, "dg must be given exactly when g is");
+    if (!workspace) return fail(H3_ERR_ARG, "workspace is NULL");
+    if (n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no tokens", (long long)n_tokens);
+    if (n_tokens > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens = %lld exceeds 2^31-1", (long long)n_tokens);
+    if (n_heads < 1 || n_heads > H3_MAX_HEADS)
+        return fail(H3_ERR_EMPTY_PARTITION, "n_heads = %d; legal values are 1..%d", n_heads, H3_MAX_HEADS);
+    if (head_dim != H3_HEAD_DIM)
+        return fail(H3_ERR_UNSUPPORTED, "head_dim = %d; only %d is supported", head_dim, H3_HEAD_DIM);
+    if (!(scale > 0.f) || scale != scale || scale > 1e30f)
+        return fail(H3_ERR_ARG, "scale must be a positive finite number");
+    h3_status st = check_segments(cu, n_segments, n_tokens, true);
+    if (st != H3_OK) return st;
+    const int64_t rows = n_tokens * n_heads;
+    if ((uint64_t)rows > UINT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens * n_heads exceeds 2^32-1");
+    const int64_t need = h3_packed_attn_backward_workspace(n_tokens, n_heads, g != nullptr);
+    if (workspace_bytes < need)
+        return fail(H3_ERR_ARG, "workspace of %lld bytes is too small: %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    const uint64_t bytes = (uint64_t)rows * head_dim * 2;
+    std::vector<Range> ins{range_of(q, bytes, "q", 0), range_of(k, bytes, "k", 0), range_of(v, bytes, "v", 0),
+                           range_of(o, bytes, "o", 0), range_of(dout, bytes, "dout", 0),
+                           range_of(lse, (uint64_t)rows * 4, "lse", 0)};
+    if (g) ins.push_back(range_of(g, bytes, "g", 0));
+    std::vector<Range> outs{range_of(dq, bytes, "dq", 0), range_of(dk, bytes, "dk", 0), range_of(dv, bytes, "dv", 0),
+                            range_of(workspace, (uint64_t)need, "workspace", 0)};
+    if (dg) outs.push_back(range_of(dg, bytes, "dg", 0));
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+
+    std::vector<int> order(n_segments);
+    for (int s = 0; s < n_segments; ++s) order[s] = s;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return cu[x + 1] - cu[x] > cu[y + 1] - cu[y]; });
+    h3::AttnBwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
+    a.delta = static_cast<float *>(workspace);
+    a.e = g ? static_cast<void *>(static_cast<char *>(workspace) + bwd_delta_bytes(rows)) : const_cast<void *>(dout);
+    a.n_heads = (uint32_t)n_heads;
+    a.n_rows = (uint32_t)rows;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.n_entries = n_segments;
+    h3::AttnBwdArgs akv = a;                          // same arguments, work list over key blocks
+    int64_t total_q = 0, total_kv = 0;
+    double pairs = 0.0;
+    for (int e = 0; e < n_segments; ++e) {
+        const int s = order[e];
+        const int64_t len = cu[s + 1] - cu[s];
+        a.wg_prefix[e] = (int32_t)total_q;
+        akv.wg_prefix[e] = (int32_t)total_kv;
+        a.seg_begin[e] = akv.seg_begin[e] = (int32_t)cu[s];
+        a.seg_len[e] = akv.seg_len[e] = (int32_t)len;
+        total_q += ((len + h3::kBwdQBlock - 1) / h3::kBwdQBlock) * n_heads;
+        total_kv += ((len + h3::kBwdKBlock - 1) / h3::kBwdKBlock) * n_heads;
+        pairs += (double)n_heads * (double)len * (double)len;
+    }
+    a.wg_prefix[n_segments] = (int32_t)total_q;
+    akv.wg_prefix[n_segments] = (int32_t)total_kv;
+    if (total_q > INT32_MAX || total_kv > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "too many work tiles");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int gx_pre = 0;
+    hipError_t e = h3::launch_attn_bwd_pre(a, s, &gx_pre);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "attention backward row-term launch failed: %s", hipGetErrorString(e));
+    e = h3::launch_attn_bwd_dkdv(akv, (int)total_kv, s);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "attention backward dk/dv launch failed: %s", hipGetErrorString(e));
+    e = h3::launch_attn_bwd_dq(a, (int)total_q, s);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "attention backward dq launch failed: %s", hipGetErrorString(e));
+    if (info) {
+        info->launches = 3;
+        info->chunks = 1;
+        info->grid_x = (int32_t)std::max<int64_t>(std::max<int64_t>(gx_pre, total_kv), total_q);
+        info->block_x = h3::kBwdThreads;
+        info->tiles = total_q + total_kv;
+        // algorithmic work: the five products S, dP, dV, dK, dQ of every same-segment (query, key) pair
+        info->flops = 10.0 * head_dim * pairs;
+        info->bytes_read = (int64_t)(bytes * (g ? 7 : 6) + (uint64_t)rows * 4);
+        info->bytes_written = (int64_t)(bytes * (g ? 4 : 3));
+    }
+    return ok();
+}
+
 h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,
                            const void *gate, void *y, int64_t tok_begin, int64_t tok_end, int32_t channels,
                            const int64_t *cu, int32_t n_segments, float eps, void *stream, h3_plan_info *info) {

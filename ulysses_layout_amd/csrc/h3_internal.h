@@ -101,4 +101,30 @@ constexpr int kAttnThreads = 512;      // 8 waves
 
 hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s);
 
+// ---- attention backward ------------------------------------------------------
+constexpr int kBwdQBlock = 256;       // queries per workgroup of the dq kernel (8 waves x 32)
+constexpr int kBwdKBlock = 128;       // keys per workgroup of the dk/dv kernel (4 key blocks x 32)
+constexpr int kBwdThreads = 512;
+constexpr int kBwdPreRowsPerWg = 16;  // (token, head) rows per workgroup of the row-term kernel
+
+struct AttnBwdArgs {
+    const void *q, *k, *v, *g, *o, *dout;
+    const float *lse;       // natural log, [N][H]
+    void *dq, *dk, *dv, *dg;
+    void *e;                // bf16 [N][H][128]: dout * sig(g) in the workspace, or dout itself when ungated
+    float *delta;           // fp32 [N][H] in the workspace
+    uint32_t n_heads;
+    uint32_t n_rows;        // N * H
+    float scale;
+    float scale_log2;       // scale * log2(e)
+    int32_t n_entries;
+    int32_t wg_prefix[kMaxSegments + 1];
+    int32_t seg_begin[kMaxSegments];
+    int32_t seg_len[kMaxSegments];
+};
+
+hipError_t launch_attn_bwd_pre(const AttnBwdArgs &a, hipStream_t s, int *grid_x);
+hipError_t launch_attn_bwd_dkdv(const AttnBwdArgs &a, int n_workgroups, hipStream_t s);
+hipError_t launch_attn_bwd_dq(const AttnBwdArgs &a, int n_workgroups, hipStream_t s);
+
 }  // namespace h3

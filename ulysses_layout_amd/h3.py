@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3
 
 # names every build of libh3.so must export (the declarations of include/h3.h)
 EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
-           "h3_packed_attn_lse", "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
+           "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_packed_attn_backward_workspace",
+           "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
            "h3_version")
 
 
@@ -84,12 +85,16 @@ def _load() -> ctypes.CDLL:
     lib.h3_head2seq_backward.argtypes = [lp, vp, ctypes.POINTER(vp), vp, ip]
     lib.h3_packed_attn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_packed_attn_lse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
+    lib.h3_packed_attn_backward.argtypes = [vp] * 11 + [vp, i64, i64, i32, i32, i64p, i32, f32, vp, ip]
+    lib.h3_packed_attn_backward_workspace.argtypes = [i64, i32, i32]
+    lib.h3_packed_attn_backward_workspace.restype = i64
     lib.h3_adaln_segment.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, i64p, i32, f32, vp, ip]
     lib.h3_partition.argtypes = [i64, i32, i32, i64p, i64p]
     lib.h3_clip_segments.argtypes = [i64p, i32, i64, i64, ctypes.POINTER(i32), i64p, i64p]
     lib.h3_clip_segments.restype = i32
     for name in ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward",
-                 "h3_packed_attn", "h3_packed_attn_lse", "h3_adaln_segment", "h3_partition"):
+                 "h3_packed_attn", "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_adaln_segment",
+                 "h3_partition"):
         getattr(lib, name).restype = ctypes.c_int
     lib.h3_status_string.argtypes = [ctypes.c_int]
     lib.h3_status_string.restype = ctypes.c_char_p
@@ -291,6 +296,37 @@ def packed_attn(q, k, v, g, o, cu_seqlens: Sequence[int], scale: float, stream=N
         lp = _dev_f32(lse, "lse", (n, h))
         _check(_lib.h3_packed_attn_lse(ptrs[0], ptrs[1], ptrs[2], gp, op, lp, n, h, d, cu, len(cu_seqlens) - 1,
                                        float(scale), _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def packed_attn_backward_workspace(n_tokens: int, n_heads: int, gated: bool) -> int:
+    """Bytes of device scratch ``packed_attn_backward`` needs."""
+    return int(_lib.h3_packed_attn_backward_workspace(int(n_tokens), int(n_heads), int(bool(gated))))
+
+
+def packed_attn_backward(q, k, v, g, o, dout, lse, dq, dk, dv, dg, workspace, cu_seqlens: Sequence[int],
+                         scale: float, stream=None) -> PlanInfo:
+    """Gradients of ``packed_attn``: dq, dk, dv (and dg when ``g`` is given).
+
+    ``o`` and ``lse`` come from the forward (``packed_attn(..., lse=lse)``);
+    ``workspace`` is a uint8 device tensor of at least
+    ``packed_attn_backward_workspace(N, H, g is not None)`` bytes.
+    """
+    torch = _torch()
+    n, h, d = q.shape
+    shp = (n, h, d)
+    ins = [_dev_bf16(t, nm, shp) for t, nm in ((q, "q"), (k, "k"), (v, "v"))]
+    gp = None if g is None else _dev_bf16(g, "g", shp)
+    op, dop = _dev_bf16(o, "o", shp), _dev_bf16(dout, "dout", shp)
+    lp = _dev_f32(lse, "lse", (n, h))
+    outs = [_dev_bf16(t, nm, shp) for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    dgp = None if dg is None else _dev_bf16(dg, "dg", shp)
+    wp = _dev_tensor(workspace, "workspace", torch.uint8)
+    cu = _i64_array(cu_seqlens)
+    info = _PlanInfo()
+    _check(_lib.h3_packed_attn_backward(ins[0], ins[1], ins[2], gp, op, dop, lp, outs[0], outs[1], outs[2], dgp, wp,
+                                        workspace.numel(), n, h, d, cu, len(cu_seqlens) - 1, float(scale),
+                                        _stream_ptr(stream), ctypes.byref(info)))
     return _info(info)
 
 
