@@ -10,8 +10,9 @@ ranks, one rank's share of 14 heads.
 
 Prints ONE JSON line.  ``value`` is the packed-attention throughput in TFLOP/s
 (algorithmic FLOPs of the step's attention / time of its attention launch);
-relayout and AdaLN rates are reported under ``components``; the relayout
-adjoints of the backward pass, timed after the step, under ``backward``.
+relayout and AdaLN rates are reported under ``components``; the backward
+pass (relayout adjoints and attention backward), timed after the step, under
+``backward``.
 ``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
@@ -129,9 +130,10 @@ def cpu_baseline(step, workload, budget_s: float):
 
 
 def measure_backward(step, reps: int = 5) -> dict:
-    """The relayout adjoints (backward of seq2head and head2seq) at the same
-    workload and plan, timed with HIP events after the timed steps.  They are
-    reported beside the step, not folded into ``value``."""
+    """The backward of the path at the same workload and plan, timed with HIP
+    events after the timed steps: the relayout adjoints (backward of seq2head
+    and head2seq) and the attention backward of one attended rank's heads.
+    They are reported beside the step, not folded into ``value``."""
     import torch
 
     import ulysses_layout_amd as h3
@@ -165,6 +167,40 @@ def measure_backward(step, reps: int = 5) -> dict:
         out[name] = {"ms": ms, "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes,
                      "launches": plan.launches}
     del grad_src
+
+    # attention backward for the first attended rank: forward with the row
+    # log-sum-exp, then dq, dk, dv (dg) from a seeded upstream gradient
+    from synth.inputs import normal_bf16
+    j = step.attn_ranks[0]
+    b = step.rank_bufs[j]
+    g = b[3] if step.gated else None
+    o = step.attn_out[j]
+    n, h, _ = o.shape
+    lse = torch.empty((n, h), dtype=torch.float32, device="cuda")
+    h3.packed_attn(b[0], b[1], b[2], g, o, step.cu, step.scale, lse=lse, stream=st)
+    dout = normal_bf16(o.shape, seed=4242, device="cuda")
+    grads = [torch.empty_like(o) for _ in range(4 if step.gated else 3)]
+    ws = torch.empty(h3.packed_attn_backward_workspace(n, h, step.gated), dtype=torch.uint8, device="cuda")
+
+    def attn_bwd():
+        return h3.packed_attn_backward(b[0], b[1], b[2], g, o, dout, lse, grads[0], grads[1], grads[2],
+                                       grads[3] if step.gated else None, ws, step.cu, step.scale, stream=st)
+
+    attn_bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    info = None
+    for a, e in ev:
+        a.record(st)
+        info = attn_bwd()
+        e.record(st)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(e) for a, e in ev) / reps
+    tflops = info.flops / (ms * 1e-3) / 1e12
+    out["attention_backward"] = {"ms": ms, "TFLOPs": tflops, "frac_bf16": tflops / PEAK_BF16_TFLOPS,
+                                 "flops": info.flops, "launches": info.launches, "heads": h, "gated": step.gated,
+                                 "flops_rule": "10 * head_dim per (query, key) pair per head"}
+    del grads, ws, dout, lse
     return out
 
 
