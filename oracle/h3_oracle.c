@@ -390,6 +390,10 @@ int h3o_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 /*   MODULATE (mode 0): y = (x - mean) / sqrt(var + eps) * (1 + scale_s)    */
 /*                      + shift_s, mean and biased var over the channels;   */
 /*   GATE     (mode 1): y = x + gate_s * b.                                 */
+/*   GATE then MODULATE (mode 2): the residual x + gate_s * b of one         */
+/*                      sub-block, modulated by the next sub-block's        */
+/*                      shift_s / scale_s (the chain the pages' clipped     */
+/*                      table serves; the residual itself is mode 1).       */
 /* Parameters are rows of [n_segments][channels], picked by GLOBAL id s.    */
 /*                                                                          */
 /* x, b: [n_local][channels].  rows: local row indices to evaluate.         */
@@ -413,6 +417,28 @@ typedef struct {
     int status;
 } adaln_job;
 
+/* LayerNorm of the fp64 row v (mean and biased variance over its C values),
+ * then * (1 + scale[s]) + shift[s], in place. */
+static void modulate_row(const adaln_job *J, int32_t s, double *v) {
+    const int32_t C = J->channels;
+    double mean = 0.0;
+    for (int32_t c = 0; c < C; ++c) mean += v[c];
+    mean /= C;
+    double var = 0.0;
+    for (int32_t c = 0; c < C; ++c) {
+        double dev = v[c] - mean;
+        var += dev * dev;
+    }
+    var /= C;
+    double inv = 1.0 / sqrt(var + J->eps);
+    for (int32_t c = 0; c < C; ++c) {
+        double xhat = (v[c] - mean) * inv;
+        double sc = bf16_bits_to_double(J->scale[(int64_t)s * C + c]);
+        double sh = bf16_bits_to_double(J->shift[(int64_t)s * C + c]);
+        v[c] = xhat * (1.0 + sc) + sh;
+    }
+}
+
 static void adaln_one(const adaln_job *J, int64_t r) {
     const int64_t i = J->rows[r];
     const int32_t C = J->channels;
@@ -425,29 +451,16 @@ static void adaln_one(const adaln_job *J, int64_t r) {
         return;
     }
     const uint16_t *xr = J->x + i * C;
-    if (J->mode == 0) {
-        double mean = 0.0;
-        for (int32_t c = 0; c < C; ++c) mean += bf16_bits_to_double(xr[c]);
-        mean /= C;
-        double var = 0.0;
-        for (int32_t c = 0; c < C; ++c) {
-            double dev = bf16_bits_to_double(xr[c]) - mean;
-            var += dev * dev;
-        }
-        var /= C;
-        double inv = 1.0 / sqrt(var + J->eps);
-        for (int32_t c = 0; c < C; ++c) {
-            double xhat = (bf16_bits_to_double(xr[c]) - mean) * inv;
-            double sc = bf16_bits_to_double(J->scale[(int64_t)s * C + c]);
-            double sh = bf16_bits_to_double(J->shift[(int64_t)s * C + c]);
-            y[c] = xhat * (1.0 + sc) + sh;
-        }
-    } else {
+    if (J->mode == 0) {              /* modulation of x */
+        for (int32_t c = 0; c < C; ++c) y[c] = bf16_bits_to_double(xr[c]);
+        modulate_row(J, s, y);
+    } else {                         /* residual gating x + gate[s] * b ... */
         const uint16_t *br = J->b + i * C;
         for (int32_t c = 0; c < C; ++c) {
             double gt = bf16_bits_to_double(J->gate[(int64_t)s * C + c]);
             y[c] = bf16_bits_to_double(xr[c]) + gt * bf16_bits_to_double(br[c]);
         }
+        if (J->mode == 2) modulate_row(J, s, y);   /* ... then the next sub-block's modulation of it */
     }
 }
 
@@ -472,9 +485,9 @@ int h3o_adaln_rows(int32_t mode, const uint16_t *x, const uint16_t *b,
                    int32_t n_entries, double eps,
                    const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads) {
     if (!x || !out || channels < 1 || n_entries < 0 || (n_rows > 0 && !rows)) return -1;
-    if (mode == 0 && (!shift || !scale)) return -1;
-    if (mode == 1 && (!b || !gate)) return -1;
-    if (mode != 0 && mode != 1) return -1;
+    if (mode != 0 && mode != 1 && mode != 2) return -1;
+    if (mode != 1 && (!shift || !scale)) return -1;
+    if (mode != 0 && (!b || !gate)) return -1;
     for (int64_t r = 0; r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= n_local) return -1;
     adaln_job J;

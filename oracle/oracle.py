@@ -264,6 +264,68 @@ def head2seq_backward(grad: np.ndarray, world: int, ranks: Optional[Sequence[int
 # attention
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# ragged collectives of the token-sharded blocks, simulated rank by rank
+# ---------------------------------------------------------------------------
+
+def reduce_scatter(partials: Sequence[np.ndarray], bias: Optional[np.ndarray] = None,
+                   ranks: Optional[Sequence[int]] = None) -> dict:
+    """Ragged reduce-scatter of per-rank partial outputs, bias added once.
+
+    "Distributed H3 Execution", Partition Contract (tensor mode): every rank
+    computes a partial output for all token rows, a ragged reduce-scatter sums
+    the partials and hands each rank the rows of its own token interval
+    (quotient/remainder split), and the projection bias, left out of the
+    partials, is added exactly once after the reduction.  Simulated message by
+    message: rank ``j`` sends rank ``i`` its partial rows ``[a_i, b_i)``; rank
+    ``i`` adds the messages in source-rank order, then the bias.
+
+    ``partials``: P arrays ``[N, C]`` of bf16 bits (or floats); ``bias``:
+    ``[C]`` bf16 bits or None.  Returns ``{i: fp64 [N_i, C]}``.
+    """
+    world = len(partials)
+    n, c = partials[0].shape
+    for j, a in enumerate(partials):
+        if a.shape != (n, c):
+            raise ValueError(f"partial {j} has shape {a.shape}, expected {(n, c)}")
+    if bias is not None and bias.shape != (c,):
+        raise ValueError(f"bias has shape {bias.shape}, expected {(c,)}")
+    tokens = partition(n, world)
+    wide = lambda a: bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)  # noqa: E731
+    out = {}
+    for i in (range(world) if ranks is None else ranks):
+        a, cnt = tokens[i]
+        acc = np.zeros((cnt, c), np.float64)
+        for j in range(world):                      # the message from rank j
+            acc += wide(partials[j][a:a + cnt])
+        if bias is not None:
+            acc += wide(bias)[None, :]              # once, after the reduction
+        out[i] = acc
+    return out
+
+
+def gather_rows(shards: Sequence[np.ndarray], pad_value: int = 0xFFFF) -> np.ndarray:
+    """Ragged row gather with the collective's temporary padding removed.
+
+    "Distributed H3 Execution", introduction: the collective that gathers the
+    ragged token shards pads them to a common size, and that padding is
+    removed before any model operation.  Simulated literally: every rank pads
+    its ``[N_i, C]`` rows to ``M = max N_i`` with ``pad_value`` rows, the
+    gather lays the P padded blocks end to end (``[P * M, C]``), and the first
+    ``N_i`` rows of block ``i`` are kept.  Returns ``[sum N_i, C]``.
+    """
+    world = len(shards)
+    c = shards[0].shape[1]
+    m = max(a.shape[0] for a in shards)
+    blocks = []
+    for a in shards:
+        pad = np.full((m - a.shape[0], c), pad_value, dtype=a.dtype)
+        blocks.append(np.concatenate([a, pad], axis=0))
+    gathered = np.concatenate(blocks, axis=0)
+    keep = [i * m + r for i in range(world) for r in range(shards[i].shape[0])]
+    return gathered[keep]
+
+
 def _u16(a: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16:
@@ -413,6 +475,7 @@ def attention_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Optional[np.
 
 MODULATE = 0
 GATE_RESIDUAL = 1
+GATE_MODULATE = 2          # the gated residual, modulated by the next sub-block's parameters
 
 
 def adaln_rows(mode: int, x: np.ndarray, b: Optional[np.ndarray], shift: Optional[np.ndarray],
@@ -453,6 +516,21 @@ def adaln_rows(mode: int, x: np.ndarray, b: Optional[np.ndarray], shift: Optiona
     return out
 
 
+def adaln_gate_modulate(x: np.ndarray, b: np.ndarray, gate: np.ndarray, shift: np.ndarray, scale: np.ndarray,
+                        tok_begin: int, tok_end: int, cu: Sequence[int], eps: float,
+                        rows: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+    """Residual gating of one sub-block followed by the next sub-block's
+    modulation, on the local rows of ``[tok_begin, tok_end)``.
+
+    Returns ``(resid, y)``: ``resid = x + gate_s * b`` (mode GATE_RESIDUAL) and
+    ``y`` = LayerNorm(resid) * (1 + scale_s) + shift_s (mode GATE_MODULATE),
+    both fp64, with the clipped table of :func:`adaln_rows`.
+    """
+    resid = adaln_rows(GATE_RESIDUAL, x, b, None, None, gate, tok_begin, tok_end, cu, eps, rows, threads)
+    y = adaln_rows(GATE_MODULATE, x, b, shift, scale, gate, tok_begin, tok_end, cu, eps, rows, threads)
+    return resid, y
+
+
 def attention_flops(cu: Sequence[int], n_heads: int, head_dim: int) -> int:
     """Algorithmic FLOPs of segment-masked attention: two products of 2*D per pair."""
     return 4 * head_dim * n_heads * sum((int(cu[s + 1]) - int(cu[s])) ** 2 for s in range(len(cu) - 1))
@@ -460,5 +538,6 @@ def attention_flops(cu: Sequence[int], n_heads: int, head_dim: int) -> int:
 
 __all__ = ["build", "partition", "clip_segments", "seq2head", "head2seq", "seq2head_backward",
            "head2seq_backward", "attention_rows", "attention_backward",
-           "attention_dense", "adaln_rows", "bf16_bits_to_f64", "EmptyPartition", "MODULATE",
-           "GATE_RESIDUAL", "default_threads", "attention_flops"]
+           "attention_dense", "adaln_rows", "adaln_gate_modulate", "reduce_scatter", "gather_rows",
+           "bf16_bits_to_f64", "EmptyPartition", "MODULATE", "GATE_RESIDUAL", "GATE_MODULATE",
+           "default_threads", "attention_flops"]

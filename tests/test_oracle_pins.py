@@ -549,3 +549,136 @@ def test_adaln_per_rank_equals_global(mode):
         part = oracle.adaln_rows(mode, x[a:a + cnt], b[a:a + cnt], shift, scale, gate, a, a + cnt,
                                  w.cu, 1e-6)
         assert np.array_equal(part, whole[a:a + cnt])
+
+
+def test_adaln_gate_modulate_matches_library_layer_norm():
+    """The residual x + gate_s * b, then the next sub-block's modulation of it,
+    against torch's fp64 layer_norm of the same residual."""
+    cu = [0, 96, 256, 512]
+    n, c = 512, 256
+    x, b, shift, scale, gate = _adaln_inputs(n, c, 3, seed=121)
+    eps = 1e-6
+    f = oracle.bf16_bits_to_f64
+    for a, e in [(0, 512), (256, 512), (100, 300)]:
+        resid, y = oracle.adaln_gate_modulate(x[a:e], b[a:e], gate, shift, scale, a, e, cu, eps)
+        seg = np.array([_segment_of_token(cu, t) for t in range(a, e)])
+        r_ref = torch.from_numpy(f(x[a:e])) + torch.from_numpy(f(gate)[seg]) * torch.from_numpy(f(b[a:e]))
+        np.testing.assert_allclose(resid, r_ref.numpy(), rtol=0, atol=1e-15)
+        ln = torch.nn.functional.layer_norm(r_ref, (c,), eps=eps).numpy()
+        np.testing.assert_allclose(y, ln * (1.0 + f(scale)[seg]) + f(shift)[seg], rtol=0, atol=1e-12)
+
+
+def test_adaln_gate_modulate_closed_forms():
+    cu = [0, 9, 30]
+    n, c = 30, 64
+    x, b, shift, scale, gate = _adaln_inputs(n, c, 2, seed=131)
+    # zero gate: the residual is x, so the chain is plain modulation of x
+    resid, y = oracle.adaln_gate_modulate(x, b, np.zeros_like(gate), shift, scale, 0, n, cu, 1e-6)
+    assert np.array_equal(resid, oracle.bf16_bits_to_f64(x))
+    assert np.array_equal(y, oracle.adaln_rows(oracle.MODULATE, x, None, shift, scale, None, 0, n, cu, 1e-6))
+    # unit gate and b = 5 - x on small integers: a constant residual row, so y is exactly shift_s
+    xi = torch.randint(-8, 9, (n, c), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    bi = (5 - xi.float()).to(torch.bfloat16)
+    as_bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    one = np.full_like(gate, 0x3F80)
+    resid, y = oracle.adaln_gate_modulate(as_bits(xi), as_bits(bi), one, shift, scale, 0, n, cu, 1e-6)
+    assert np.array_equal(resid, np.full((n, c), 5.0))
+    sh = oracle.bf16_bits_to_f64(shift)
+    assert np.array_equal(y[:9], np.broadcast_to(sh[0], (9, c)))
+    assert np.array_equal(y[9:], np.broadcast_to(sh[1], (21, c)))
+
+
+def test_adaln_gate_modulate_per_rank_equals_global():
+    w = WORKLOADS["8k_p6"]
+    n, c = w.n_tokens, 64
+    x, b, shift, scale, gate = _adaln_inputs(n, c, w.n_segments, seed=141)
+    r_all, y_all = oracle.adaln_gate_modulate(x, b, gate, shift, scale, 0, n, w.cu, 1e-6)
+    for a, cnt in oracle.partition(n, w.world):
+        r, y = oracle.adaln_gate_modulate(x[a:a + cnt], b[a:a + cnt], gate, shift, scale, a, a + cnt, w.cu, 1e-6)
+        assert np.array_equal(r, r_all[a:a + cnt]) and np.array_equal(y, y_all[a:a + cnt])
+
+
+# ---------------------------------------------------------------------------
+# ragged reduce-scatter and row gather
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("world", [1, 2, 3, 6, 8])
+def test_reduce_scatter_is_sum_then_numpy_split(world):
+    """Rank i's rows of (sum of the partials + bias), with numpy's array_split
+    (first N mod P parts one larger) as the independent row split."""
+    n, c = 1003, 24
+    parts = [normal_bf16_bits((n, c), seed=150 + j) for j in range(world)]
+    bias = normal_bf16_bits((c,), seed=149)
+    got = oracle.reduce_scatter(parts, bias)
+    total = sum(oracle.bf16_bits_to_f64(p) for p in parts) + oracle.bf16_bits_to_f64(bias)
+    for i, ref in enumerate(np.array_split(total, world)):
+        np.testing.assert_allclose(got[i], ref, rtol=0, atol=1e-12)
+
+
+def test_reduce_scatter_adds_bias_once():
+    n, c, world = 37, 16, 4
+    bias = normal_bf16_bits((c,), seed=160)
+    zero = [np.zeros((n, c), np.uint16) for _ in range(world)]
+    got = oracle.reduce_scatter(zero, bias)
+    assert sum(v.shape[0] for v in got.values()) == n
+    for i, v in got.items():
+        assert np.array_equal(v, np.broadcast_to(oracle.bf16_bits_to_f64(bias), v.shape))
+    same = [normal_bf16_bits((n, c), seed=161)] * world
+    got = oracle.reduce_scatter(same, None, ranks=[2])
+    a, cnt = oracle.partition(n, world)[2]
+    assert np.array_equal(got[2], world * oracle.bf16_bits_to_f64(same[0][a:a + cnt]))
+    assert list(got) == [2]
+
+
+def test_gather_rows_inverts_numpy_split():
+    rng = np.random.default_rng(170)
+    for world in (1, 2, 3, 5, 8):
+        for n in (world, 17, 64, 1001):
+            if n < world:
+                continue
+            x = rng.integers(0, 0x7F00, size=(n, 8), dtype=np.uint16)    # never the 0xFFFF padding rows
+            assert np.array_equal(oracle.gather_rows(np.array_split(x, world)), x), (world, n)
+
+
+def _free_port():
+    import socket
+    with socket.socket() as s:
+        s.bind(("127.0.0.1", 0))
+        return s.getsockname()[1]
+
+
+def _gloo_worker(rank, world, port, tmp):
+    import torch.distributed as dist
+    dist.init_process_group("gloo", init_method=f"tcp://127.0.0.1:{port}", rank=rank, world_size=world)
+    n, c = 101, 8
+    # the reduce-scatter of this rank's fp64 partial, rows split by torch.tensor_split
+    part = torch.from_numpy(oracle.bf16_bits_to_f64(normal_bf16_bits((n, c), seed=180 + rank)))
+    chunks = list(torch.tensor_split(part, world))
+    out = torch.empty_like(chunks[rank])
+    dist.reduce_scatter(out, chunks)
+    np.save(os.path.join(tmp, f"rs{rank}.npy"), out.numpy())
+    # the padded all-gather of this rank's token shard, then the padding stripped
+    x = torch.from_numpy(normal_bf16_bits((n, c), seed=190).astype(np.int32))
+    shard = torch.tensor_split(x, world)[rank]
+    m = -(-n // world)
+    padded = torch.cat([shard, torch.full((m - shard.shape[0], c), -1, dtype=torch.int32)])
+    blocks = [torch.empty_like(padded) for _ in range(world)]
+    dist.all_gather(blocks, padded)
+    sizes = [t.shape[0] for t in torch.tensor_split(x, world)]
+    np.save(os.path.join(tmp, f"ag{rank}.npy"), torch.cat([b[:s] for b, s in zip(blocks, sizes)]).numpy())
+    dist.destroy_process_group()
+
+
+def test_reduce_scatter_and_gather_match_gloo_collectives(tmp_path):
+    """Three gloo processes on the CPU: torch.distributed's ragged
+    reduce_scatter and padded all_gather give what the oracle simulates."""
+    import torch.multiprocessing as mp
+    world, n, c = 3, 101, 8
+    mp.spawn(_gloo_worker, args=(world, _free_port(), str(tmp_path)), nprocs=world)
+    parts = [normal_bf16_bits((n, c), seed=180 + j) for j in range(world)]
+    ref = oracle.reduce_scatter(parts, None)
+    x = normal_bf16_bits((n, c), seed=190)
+    shards = [x[a:a + cnt] for a, cnt in oracle.partition(n, world)]
+    for i in range(world):
+        np.testing.assert_allclose(np.load(tmp_path / f"rs{i}.npy"), ref[i], rtol=0, atol=1e-12)
+        assert np.array_equal(np.load(tmp_path / f"ag{i}.npy"), oracle.gather_rows(shards).astype(np.int32))
