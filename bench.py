@@ -12,7 +12,8 @@ Prints ONE JSON line.  ``value`` is the packed-attention throughput in TFLOP/s
 (algorithmic FLOPs of the step's attention / time of its attention launch);
 relayout and AdaLN rates are reported under ``components``; the backward
 pass (relayout adjoints and attention backward), timed after the step, under
-``backward``.
+``backward``; the gated AdaLN chain, the ragged reduce-scatter and the ragged
+row gather, also timed after the step, under ``token_sharded_ops``.
 ``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
@@ -204,6 +205,64 @@ def measure_backward(step, reps: int = 5) -> dict:
     return out
 
 
+def measure_next(step, reps: int = 5) -> dict:
+    """The token-sharded blocks' ops at the same workload, timed with HIP
+    events after the timed steps (not part of ``value``): the gated AdaLN chain
+    over every rank interval (x, branch -> residual, modulated y), the ragged
+    reduce-scatter of P partial outputs [N, C] with bias for every rank, and
+    the ragged row gather of the P token shards back to [N, C]."""
+    import torch
+
+    import ulysses_layout_amd as h3
+    from synth.inputs import normal_bf16
+
+    st = torch.cuda.current_stream()
+    n, c, world = step.n_tokens, step.channels, step.world
+    row = c * 2
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        infos = None
+        for a, e in ev:
+            a.record(st)
+            infos = fn()
+            e.record(st)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(e) for a, e in ev) / reps, infos
+
+    def entry(ms, nbytes, launches):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": ms, "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes, "launches": launches}
+
+    branch = normal_bf16((n, c), seed=4300, device="cuda")
+    resid, y = torch.empty_like(branch), torch.empty_like(branch)
+
+    def chain():
+        return [h3.adaln_gate_modulate(step.x[a:a + cnt], branch[a:a + cnt], step.gate, step.shift, step.ada_scale,
+                                       resid[a:a + cnt], y[a:a + cnt], a, a + cnt, step.cu, step.eps, stream=st)
+                for a, cnt in step.tokens]
+
+    ms, infos = timed(chain)
+    out["adaln_gate_modulate"] = entry(ms, 4 * n * row, len(infos))
+    del resid, y
+
+    partials = [branch] + [normal_bf16((n, c), seed=4301 + j, device="cuda") for j in range(1, world)]
+    bias = normal_bf16((c,), seed=4299, device="cuda")
+    shards = [torch.empty((cnt, c), dtype=torch.bfloat16, device="cuda") for _, cnt in step.tokens]
+    ms, info = timed(lambda: h3.reduce_scatter(partials, bias, shards, stream=st))
+    out["reduce_scatter"] = entry(ms, (world + 1) * n * row, info.launches)
+    out["reduce_scatter"]["partials"] = world
+    del partials
+    dst = torch.empty((n, c), dtype=torch.bfloat16, device="cuda")
+    ms, info = timed(lambda: h3.gather_rows(shards, dst, stream=st))
+    out["gather_rows"] = entry(ms, 2 * n * row, info.launches)
+    del shards, dst, branch
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -264,6 +323,7 @@ def main():
     launch_ms = ms["attention"] / attn_launches
     traffic = read_traffic(flops_per_launch)
     backward = measure_backward(step)
+    next_ops = measure_next(step)
 
     components = {
         "seq2head": {"ms": ms["seq2head"], "GBps": s2h_gbps, "frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
@@ -307,6 +367,7 @@ def main():
         / 1e9 / PEAK_HBM_GBPS,
         "components": components,
         "backward": backward,
+        "token_sharded_ops": next_ops,
         "roofline": {
             "kernel": ATTN_KERNEL,
             "bound": "mfma",

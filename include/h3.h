@@ -255,6 +255,81 @@ h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, cons
                            void *stream, h3_plan_info *info);
 
 /* ------------------------------------------------------------------------
+ * h3_adaln_gate_modulate -- one sub-block's gated residual followed by the
+ * next sub-block's modulation, in one pass over the rows.
+ *
+ * [DIST] Partition Contract: the clipped, rebased segment table serves both
+ * AdaLN modulation and residual gating; here the two are chained as a DiT
+ * block chains them.  For local row i of global segment s, with
+ * r = x + gate[s] * branch in fp32:
+ *   resid = r rounded to bf16 (stored; the same bits as
+ *           h3_adaln_segment(GATE_RESIDUAL))
+ *   y     = (r - mean)/sqrt(var + eps) * (1 + scale[s]) + shift[s]
+ *           (mean and biased var over the C channels of the fp32 r)
+ * x and branch are read once and resid is never read back (4 row streams
+ * instead of the unfused 5).  y normalises the unrounded r, so it is one
+ * rounding closer to the exact chain than MODULATE applied to the stored
+ * resid, and may differ from that in the last bits (it equals it when r is
+ * exactly representable, e.g. for a zero gate).
+ *
+ * x, branch, resid, y: device, [tok_end - tok_begin][C] bf16.
+ * gate (this sub-block), shift, scale (the next sub-block): device, [S][C].
+ * resid and y must not overlap each other or any input.
+ * cu_seqlens, channels, eps, errors: as h3_adaln_segment.  Launches: 1.
+ * ------------------------------------------------------------------------ */
+#define H3_ADALN_GATE_MODULATE 2
+h3_status h3_adaln_gate_modulate(const void *x, const void *branch, const void *gate,
+                                 const void *shift, const void *scale, void *resid, void *y,
+                                 int64_t tok_begin, int64_t tok_end, int32_t channels,
+                                 const int64_t *cu_seqlens, int32_t n_segments, float eps,
+                                 void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_reduce_scatter -- ragged reduce-scatter of per-rank partial outputs with
+ * the bias added once, the P ranks held as separate buffers on one device.
+ *
+ * [DIST] Partition Contract (tensor mode): each rank's partial output covers
+ * every token row; the reduce-scatter sums the partials and assigns each
+ * rank the rows of its token interval (h3_partition of n_tokens); the
+ * projection bias, left out of the partials, is added exactly once after
+ * the reduction.  For selected rank i and its rows [a_i, a_i + N_i):
+ *   out[i][t - a_i][c] = bf16( (sum over j = 0..P-1 of partials[j][t][c]) + bias[c] )
+ * summed in fp32 in rank order, rounded once.
+ *
+ * partials: host array of P device pointers, each [n_tokens][C] bf16.
+ * bias: device [C] bf16, or NULL for none.
+ * out: host array of P device pointers; out[i] is [N_i][C] bf16, written
+ *      iff rank i is selected (rank == -1: every rank; else only `rank`),
+ *      and may be NULL otherwise.  Outputs must not overlap any input or
+ *      each other.
+ * world: P, 1..min(n_tokens, 64) (an empty part is H3_ERR_EMPTY_PARTITION).
+ * channels: C, a multiple of 8, <= H3_MAX_CHANNELS; every pointer 16-byte
+ *      aligned.  Launches: 1.
+ * ------------------------------------------------------------------------ */
+h3_status h3_reduce_scatter(const void *const *partials, const void *bias, void *const *out,
+                            int64_t n_tokens, int32_t channels, int32_t world, int32_t rank,
+                            void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * h3_gather_rows -- ragged row gather with the collective's padding removed.
+ *
+ * [DIST] introduction: a ragged row gather pads the token shards to one size
+ * for the collective, and that temporary padding is removed before any
+ * model operation.  Rank i's N_i rows (h3_partition of n_tokens) are placed
+ * at their global rows [a_i, a_i + N_i) of dst:
+ *   dst[a_i + r][c] = shards[i][r][c],  r < N_i
+ * so rows a padded buffer holds past N_i are never read.  For a padded
+ * gathered buffer [P][M][C] pass shards[i] = buffer + i*M*C.
+ *
+ * shards: host array of P device pointers, shards[i] holding >= N_i rows of
+ *      C bf16.  dst: device [n_tokens][C] bf16, not overlapping the shards'
+ *      first N_i rows.
+ * world, channels, alignment and errors as h3_reduce_scatter.  Launches: 1.
+ * ------------------------------------------------------------------------ */
+h3_status h3_gather_rows(const void *const *shards, void *dst, int64_t n_tokens, int32_t channels,
+                         int32_t world, void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
  * Host-only helpers (no device work, callable without a GPU).
  * ------------------------------------------------------------------------ */
 

@@ -25,6 +25,18 @@ ARG, EMPTY, SEGS, UNSUP, ALIAS = 1, 2, 3, 4, 5
 FAKE = 1 << 40     # a device-looking address that is never touched
 
 
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0      # counts devices without initialising HIP
+
+
+# The rejection tests hand the library fake device addresses and rely on every
+# case being refused on the host.  Where a GPU is visible a case that slipped
+# through validation would launch on those addresses, so they run only on
+# machines without one.
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses; run where no GPU is visible")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -112,6 +124,7 @@ def _layout(**kw):
     return Layout(**base)
 
 
+@fake_addresses
 @pytest.mark.parametrize("kw,status", [
     (dict(world=0), EMPTY), (dict(world=57), EMPTY), (dict(n_tokens=3, world=4), EMPTY),
     (dict(n_tokens=0), EMPTY), (dict(head_dim=64), UNSUP), (dict(n_planes=0), ARG),
@@ -128,6 +141,7 @@ def test_seq2head_rejects_bad_layout(kw, status):
         assert "legal values are 1.." in msg
 
 
+@fake_addresses
 def test_seq2head_rejects_null_and_alias():
     lay = _layout()
     rc, _ = _seq2head(lay, src=None)
@@ -163,6 +177,7 @@ def _seq2head_bwd(layout, grad_src=FAKE, grad_dst=None):
     return LIB.h3_seq2head_backward(ctypes.byref(layout), arr, grad_src, None, ctypes.byref(info)), info
 
 
+@fake_addresses
 @pytest.mark.parametrize("kw,status", [
     (dict(world=0), EMPTY), (dict(world=57), EMPTY), (dict(n_tokens=0), EMPTY), (dict(head_dim=64), UNSUP),
     (dict(n_planes=9), ARG), (dict(rank=2), ARG), (dict(max_chunk_bytes=1000), ARG),
@@ -174,6 +189,7 @@ def test_seq2head_backward_rejects_bad_layout(kw, status):
     assert LIB.h3_last_error().decode()
 
 
+@fake_addresses
 def test_seq2head_backward_rejects_null_and_alias():
     lay = _layout()
     assert _seq2head_bwd(lay, grad_src=None)[0] == ARG
@@ -195,6 +211,7 @@ def _head2seq_bwd(layout, grad_dst=FAKE, grad_src=None):
     return LIB.h3_head2seq_backward(ctypes.byref(layout), grad_dst, arr, None, ctypes.byref(info)), info
 
 
+@fake_addresses
 @pytest.mark.parametrize("kw,status", [
     (dict(n_planes=3), ARG), (dict(world=57), EMPTY), (dict(head_dim=64), UNSUP), (dict(rank=5), ARG),
 ])
@@ -206,6 +223,7 @@ def test_head2seq_backward_rejects_bad_layout(kw, status):
     assert info.launches == 0
 
 
+@fake_addresses
 def test_head2seq_backward_rejects_null_and_alias():
     lay = _layout(n_planes=1)
     assert _head2seq_bwd(lay, grad_dst=None)[0] == ARG
@@ -213,6 +231,7 @@ def test_head2seq_backward_rejects_null_and_alias():
     assert _head2seq_bwd(lay, grad_src=[FAKE * 2, FAKE + 256])[0] == ALIAS
 
 
+@fake_addresses
 def test_rejected_call_leaves_no_state():
     rc, _ = _seq2head(_layout(world=57))
     assert rc == EMPTY
@@ -234,6 +253,7 @@ def _attn(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), g=None, o=FAKE + (3 <<
     (dict(scale=0.0), ARG), (dict(scale=float("nan")), ARG), (dict(o=FAKE + 100), ALIAS),
     (dict(g=FAKE + (3 << 32) + 64), ALIAS), (dict(cu=tuple(range(0, 2 * 300, 2)) + (600,), n=600), SEGS),
 ])
+@fake_addresses
 def test_packed_attn_rejects(kw, status):
     rc, info = _attn(**kw)
     assert rc == status, LIB.h3_last_error()
@@ -255,6 +275,7 @@ def _adaln(mode=0, x=FAKE, b=None, shift=FAKE + (1 << 32), scale=FAKE + (2 << 32
     (dict(c=16392), UNSUP), (dict(e=600), SEGS), (dict(cu=(0, 300, 200, 512)), SEGS),
     (dict(y=FAKE + 1000), ALIAS), (dict(eps=float("nan")), ARG),
 ])
+@fake_addresses
 def test_adaln_rejects(kw, status):
     rc, info = _adaln(**kw)
     assert rc == status, LIB.h3_last_error()
@@ -265,3 +286,86 @@ def test_status_strings():
     for code, name in h3.h3.STATUS_NAMES.items():
         LIB.h3_status_string.restype = ctypes.c_char_p
         assert LIB.h3_status_string(code).decode() == name
+
+
+def _chain(x=FAKE, b=FAKE + (1 << 32), gate=FAKE + (2 << 32), shift=FAKE + (3 << 32), scale=FAKE + (4 << 32),
+           resid=FAKE + (5 << 32), y=FAKE + (6 << 32), a=0, e=256, c=7168, cu=(0, 96, 256, 512), eps=1e-6):
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_adaln_gate_modulate(x, b, gate, shift, scale, resid, y, a, e, c, cua, len(cu) - 1, eps, None,
+                                    ctypes.byref(info))
+    return rc, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ARG), (dict(b=None), ARG), (dict(gate=None), ARG), (dict(shift=None), ARG),
+    (dict(scale=None), ARG), (dict(resid=None), ARG), (dict(y=None), ARG), (dict(a=5, e=5), EMPTY),
+    (dict(c=7170), UNSUP), (dict(e=600), SEGS), (dict(eps=-1.0), ARG),
+    (dict(resid=FAKE + (6 << 32) + 512), ALIAS),          # resid overlaps y
+    (dict(y=FAKE + (1 << 32) + 4096), ALIAS),             # y overlaps the branch
+    (dict(resid=FAKE + (2 << 32)), ALIAS),                # resid overlaps the gate rows
+])
+@fake_addresses
+def test_adaln_gate_modulate_rejects(kw, status):
+    rc, info = _chain(**kw)
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+def _ptrs(values):
+    return (ctypes.c_void_p * len(values))(*values)
+
+
+def _rs(n=1003, c=64, world=3, rank=-1, partials=None, out=None, bias=FAKE + (9 << 32)):
+    partials = [FAKE + (j << 32) for j in range(world)] if partials is None else partials
+    out = [FAKE + ((20 + i) << 32) for i in range(world)] if out is None else out
+    info = _PlanInfo()
+    rc = LIB.h3_reduce_scatter(_ptrs(partials), bias, _ptrs(out), n, c, world, rank, None, ctypes.byref(info))
+    return rc, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(world=0), EMPTY), (dict(world=1004), EMPTY), (dict(n=0), EMPTY), (dict(n=100, world=65), UNSUP),
+    (dict(c=60), UNSUP), (dict(c=0), UNSUP), (dict(rank=3), ARG), (dict(rank=-2), ARG),
+    (dict(partials=[FAKE, None, FAKE + (2 << 32)]), ARG), (dict(out=[FAKE + (20 << 32), None, FAKE + (22 << 32)]), ARG),
+    (dict(partials=[FAKE, FAKE + (1 << 32) + 8, FAKE + (2 << 32)]), ARG),          # misaligned
+    (dict(bias=FAKE + (9 << 32) + 2), ARG),
+    (dict(out=[FAKE + (20 << 32), FAKE + 1003 * 128 - 128, FAKE + (22 << 32)]), ALIAS),   # inside partial 0
+    (dict(out=[FAKE + (20 << 32), FAKE + (20 << 32) + 334 * 128, FAKE + (22 << 32)]), ALIAS),  # out 0 / out 1
+    (dict(bias=FAKE + (21 << 32) + 256), ALIAS),
+    (dict(n=1 << 22, c=8192, world=1), UNSUP),             # one rank's range passes 2^31 vectors
+])
+@fake_addresses
+def test_reduce_scatter_rejects(kw, status):
+    rc, info = _rs(**kw)
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+@fake_addresses
+def test_reduce_scatter_unselected_outputs_may_be_null():
+    # rank 1 only: the NULL out[0] and out[2] are not looked at; the call is
+    # refused for the selected output, which overlaps partial 0
+    rc, info = _rs(rank=1, out=[None, FAKE, None])
+    assert rc == ALIAS, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+def _gather(n=1003, c=64, world=3, shards=None, dst=FAKE + (30 << 32)):
+    shards = [FAKE + (j << 32) for j in range(world)] if shards is None else shards
+    info = _PlanInfo()
+    rc = LIB.h3_gather_rows(_ptrs(shards), dst, n, c, world, None, ctypes.byref(info))
+    return rc, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(world=0), EMPTY), (dict(world=1004), EMPTY), (dict(c=12), UNSUP), (dict(dst=None), ARG),
+    (dict(shards=[FAKE, None, FAKE]), ARG), (dict(dst=FAKE + (30 << 32) + 4), ARG),
+    (dict(dst=FAKE + (1 << 32) - 64), ALIAS),
+    (dict(shards=[FAKE, FAKE + (30 << 32) + 1003 * 128 - 16, FAKE]), ALIAS),
+])
+@fake_addresses
+def test_gather_rows_rejects(kw, status):
+    rc, info = _gather(**kw)
+    assert rc == status, LIB.h3_last_error()
+    assert info.launches == 0

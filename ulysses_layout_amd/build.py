@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3.so")
 ARCH = "gfx950"
 
-SOURCES = ["h3_api.hip", "relayout.hip", "adaln.hip", "packed_attn.hip", "attn_backward.hip"]
+SOURCES = ["h3_api.hip", "relayout.hip", "adaln.hip", "packed_attn.hip", "attn_backward.hip", "ragged.hip"]
 
 # Packed FP32 VALU forms are kept out of the generated code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

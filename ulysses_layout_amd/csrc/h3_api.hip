@@ -670,18 +670,149 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
     return ok();
 }
 
-h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,
-                           const void *gate, void *y, int64_t tok_begin, int64_t tok_end, int32_t channels,
-                           const int64_t *cu, int32_t n_segments, float eps, void *stream, h3_plan_info *info) {
+// 16-byte vector accesses need 16-byte aligned buffers.
+static h3_status check_aligned(const void *p, const char *what, int index) {
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+        return fail(H3_ERR_ARG, "%s[%d] is not 16-byte aligned", what, index);
+    return H3_OK;
+}
+
+// Shared checks of the ragged collectives: token split, channels, index range.
+static h3_status check_ragged(int64_t n_tokens, int32_t channels, int32_t world) {
+    if (n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no rows to split", (long long)n_tokens);
+    if (world < 1 || world > n_tokens)
+        return fail(H3_ERR_EMPTY_PARTITION, "world = %d would leave a rank without rows; legal values are 1..%lld",
+                    world, (long long)n_tokens);
+    if (world > h3::kMaxRanks)
+        return fail(H3_ERR_UNSUPPORTED, "world = %d; at most %d ranks are supported", world, h3::kMaxRanks);
+    if (channels < 8 || channels % 8 != 0 || channels > H3_MAX_CHANNELS)
+        return fail(H3_ERR_UNSUPPORTED, "channels = %d; must be a multiple of 8 in 8..%d", channels,
+                    H3_MAX_CHANNELS);
+    int64_t b0, c0;
+    split(n_tokens, world, 0, &b0, &c0);              // the largest rank
+    if (c0 * (channels / 8) > INT32_MAX)
+        return fail(H3_ERR_UNSUPPORTED, "a rank's %lld rows x %d channels exceed 2^31-1 16-byte vectors",
+                    (long long)c0, channels);
+    return H3_OK;
+}
+
+h3_status h3_reduce_scatter(const void *const *partials, const void *bias, void *const *out, int64_t n_tokens,
+                            int32_t channels, int32_t world, int32_t rank, void *stream, h3_plan_info *info) {
     clear_info(info);
-    if (mode != H3_ADALN_MODULATE && mode != H3_ADALN_GATE_RESIDUAL)
-        return fail(H3_ERR_ARG, "mode = %d; legal values are %d (modulate) and %d (gate residual)", mode,
-                    H3_ADALN_MODULATE, H3_ADALN_GATE_RESIDUAL);
+    h3_status st = check_ragged(n_tokens, channels, world);
+    if (st != H3_OK) return st;
+    if (!partials || !out) return fail(H3_ERR_ARG, "partials and out must be non-NULL arrays of %d pointers", world);
+    if (rank < -1 || rank >= world)
+        return fail(H3_ERR_ARG, "rank = %d; legal values are -1 (every rank) or 0..%d", rank, world - 1);
+    const uint64_t row_bytes = (uint64_t)channels * 2;
+    std::vector<Range> ins, outs;
+    for (int j = 0; j < world; ++j) {
+        if (!partials[j]) return fail(H3_ERR_ARG, "partials[%d] is NULL", j);
+        if ((st = check_aligned(partials[j], "partials", j)) != H3_OK) return st;
+        ins.push_back(range_of(partials[j], (uint64_t)n_tokens * row_bytes, "partials", j));
+    }
+    if (bias) {
+        if ((st = check_aligned(bias, "bias", 0)) != H3_OK) return st;
+        ins.push_back(range_of(bias, row_bytes, "bias", 0));
+    }
+    h3::RaggedArgs a;
+    std::memset(&a, 0, sizeof a);
+    int n_slots = 0;
+    uint32_t max_vec = 0;
+    int64_t rows_out = 0;
+    for (int i = 0; i < world; ++i) {
+        if (rank >= 0 && i != rank) continue;
+        if (!out[i]) return fail(H3_ERR_ARG, "out[%d] is NULL but rank %d is selected", i, i);
+        if ((st = check_aligned(out[i], "out", i)) != H3_OK) return st;
+        int64_t begin, count;
+        split(n_tokens, world, i, &begin, &count);
+        outs.push_back(range_of(out[i], (uint64_t)count * row_bytes, "out", i));
+        a.dst[n_slots] = out[i];
+        a.row_vec0[n_slots] = (uint64_t)begin * (channels / 8);
+        a.n_vec[n_slots] = (uint32_t)(count * (channels / 8));
+        max_vec = std::max(max_vec, a.n_vec[n_slots]);
+        rows_out += count;
+        ++n_slots;
+    }
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
+    for (int j = 0; j < world; ++j) a.src[j] = partials[j];
+    a.bias = bias;
+    a.nv_row = (uint32_t)(channels / 8);
+    if (a.nv_row >= 2) a.div_row = h3::make_fastdiv(a.nv_row);
+    a.world = world;
+    (void)hipGetLastError();
+    int gx = 0;
+    hipError_t e = h3::launch_reduce_scatter(a, n_slots, max_vec, static_cast<hipStream_t>(stream), &gx);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "reduce-scatter launch failed: %s", hipGetErrorString(e));
+    if (info) {
+        info->launches = 1;
+        info->chunks = 1;
+        info->grid_x = gx;
+        info->block_x = h3::kCopyThreads;
+        info->bytes_read = (int64_t)((uint64_t)world * rows_out * row_bytes + (bias ? row_bytes : 0));
+        info->bytes_written = (int64_t)(rows_out * row_bytes);
+        info->max_launch_src_bytes = info->bytes_read;
+        info->tiles = n_slots;
+    }
+    return ok();
+}
+
+h3_status h3_gather_rows(const void *const *shards, void *dst, int64_t n_tokens, int32_t channels, int32_t world,
+                         void *stream, h3_plan_info *info) {
+    clear_info(info);
+    h3_status st = check_ragged(n_tokens, channels, world);
+    if (st != H3_OK) return st;
+    if (!shards || !dst) return fail(H3_ERR_ARG, "shards and dst must be non-NULL");
+    if ((st = check_aligned(dst, "dst", 0)) != H3_OK) return st;
+    const uint64_t row_bytes = (uint64_t)channels * 2;
+    std::vector<Range> ins;
+    h3::RaggedArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint32_t max_vec = 0;
+    for (int i = 0; i < world; ++i) {
+        if (!shards[i]) return fail(H3_ERR_ARG, "shards[%d] is NULL", i);
+        if ((st = check_aligned(shards[i], "shards", i)) != H3_OK) return st;
+        int64_t begin, count;
+        split(n_tokens, world, i, &begin, &count);
+        ins.push_back(range_of(shards[i], (uint64_t)count * row_bytes, "shards", i));
+        a.src[i] = shards[i];
+        a.row_vec0[i] = (uint64_t)begin * (channels / 8);
+        a.n_vec[i] = (uint32_t)(count * (channels / 8));
+        max_vec = std::max(max_vec, a.n_vec[i]);
+    }
+    if ((st = check_alias(ins, {range_of(dst, (uint64_t)n_tokens * row_bytes, "dst", 0)})) != H3_OK) return st;
+    a.dst_all = dst;
+    a.nv_row = (uint32_t)(channels / 8);
+    a.world = world;
+    (void)hipGetLastError();
+    int gx = 0;
+    hipError_t e = h3::launch_gather_rows(a, world, max_vec, static_cast<hipStream_t>(stream), &gx);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "row gather launch failed: %s", hipGetErrorString(e));
+    if (info) {
+        info->launches = 1;
+        info->chunks = 1;
+        info->grid_x = gx;
+        info->block_x = h3::kCopyThreads;
+        info->bytes_read = (int64_t)((uint64_t)n_tokens * row_bytes);
+        info->bytes_written = info->bytes_read;
+        info->max_launch_src_bytes = info->bytes_read;
+        info->tiles = world;
+    }
+    return ok();
+}
+
+// The shared body of the AdaLN entry points (mode H3_ADALN_GATE_MODULATE takes
+// every parameter row and writes resid as well as y).
+static h3_status adaln_impl(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,
+                            const void *gate, void *resid, void *y, int64_t tok_begin, int64_t tok_end,
+                            int32_t channels, const int64_t *cu, int32_t n_segments, float eps, void *stream,
+                            h3_plan_info *info) {
+    clear_info(info);
+    const bool modulate = mode != H3_ADALN_GATE_RESIDUAL, gated = mode != H3_ADALN_MODULATE;
     if (!x || !y) return fail(H3_ERR_ARG, "x and y must be non-NULL");
-    if (mode == H3_ADALN_MODULATE && (!shift || !scale))
-        return fail(H3_ERR_ARG, "modulate needs shift and scale");
-    if (mode == H3_ADALN_GATE_RESIDUAL && (!branch || !gate))
-        return fail(H3_ERR_ARG, "gate residual needs branch and gate");
+    if (mode == H3_ADALN_GATE_MODULATE && !resid) return fail(H3_ERR_ARG, "resid must be non-NULL");
+    if (modulate && (!shift || !scale)) return fail(H3_ERR_ARG, "modulate needs shift and scale");
+    if (gated && (!branch || !gate)) return fail(H3_ERR_ARG, "gate residual needs branch and gate");
     if (tok_begin < 0 || tok_end <= tok_begin)
         return fail(H3_ERR_EMPTY_PARTITION, "token interval [%lld, %lld) is empty", (long long)tok_begin,
                     (long long)tok_end);
@@ -689,8 +820,7 @@ h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, cons
     if (channels < 8 || channels % 8 != 0 || channels > H3_MAX_CHANNELS)
         return fail(H3_ERR_UNSUPPORTED, "channels = %d; must be a multiple of 8 in 8..%d", channels,
                     H3_MAX_CHANNELS);
-    if (mode == H3_ADALN_MODULATE && !(eps >= 0.f && eps < 1e30f))
-        return fail(H3_ERR_ARG, "eps must be a finite number >= 0");
+    if (modulate && !(eps >= 0.f && eps < 1e30f)) return fail(H3_ERR_ARG, "eps must be a finite number >= 0");
     h3_status st = check_segments(cu, n_segments, tok_end, false);
     if (st != H3_OK) return st;
 
@@ -698,18 +828,22 @@ h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, cons
     const uint64_t row_bytes = (uint64_t)channels * 2;
     const uint64_t par_bytes = (uint64_t)n_segments * row_bytes;
     std::vector<Range> ins{range_of(x, n_rows * row_bytes, "x", 0)};
-    if (mode == H3_ADALN_MODULATE) {
+    if (modulate) {
         ins.push_back(range_of(shift, par_bytes, "shift", 0));
         ins.push_back(range_of(scale, par_bytes, "scale", 0));
-    } else {
+    }
+    if (gated) {
         ins.push_back(range_of(branch, n_rows * row_bytes, "branch", 0));
         ins.push_back(range_of(gate, par_bytes, "gate", 0));
     }
-    if ((st = check_alias(ins, {range_of(y, n_rows * row_bytes, "y", 0)})) != H3_OK) return st;
+    std::vector<Range> outs{range_of(y, n_rows * row_bytes, "y", 0)};
+    if (mode == H3_ADALN_GATE_MODULATE) outs.push_back(range_of(resid, n_rows * row_bytes, "resid", 0));
+    if ((st = check_alias(ins, outs)) != H3_OK) return st;
 
     h3::AdalnArgs a;
     std::memset(&a, 0, sizeof a);
     a.x = x; a.branch = branch; a.shift = shift; a.scale = scale; a.gate = gate; a.y = y;
+    a.resid = mode == H3_ADALN_GATE_MODULATE ? resid : nullptr;
     a.n_rows = (uint32_t)n_rows;
     a.channels = (uint32_t)channels;
     a.eps = eps;
@@ -735,14 +869,34 @@ h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, cons
         info->chunks = 1;
         info->grid_x = gx;
         info->block_x = h3::kAdalnThreads;
-        const uint64_t streams_in = mode == H3_ADALN_MODULATE ? 1 : 2;
-        info->bytes_read = (int64_t)(streams_in * n_rows * row_bytes + (mode == H3_ADALN_MODULATE ? 2 : 1) *
-                                     (uint64_t)n * row_bytes);
-        info->bytes_written = (int64_t)(n_rows * row_bytes);
+        const uint64_t streams_in = gated ? 2 : 1, params = (modulate ? 2 : 0) + (gated ? 1 : 0);
+        const uint64_t streams_out = mode == H3_ADALN_GATE_MODULATE ? 2 : 1;
+        info->bytes_read = (int64_t)(streams_in * n_rows * row_bytes + params * (uint64_t)n * row_bytes);
+        info->bytes_written = (int64_t)(streams_out * n_rows * row_bytes);
         info->max_launch_src_bytes = info->bytes_read;
         info->tiles = n;
     }
     return ok();
+}
+
+h3_status h3_adaln_segment(int32_t mode, const void *x, const void *branch, const void *shift, const void *scale,
+                           const void *gate, void *y, int64_t tok_begin, int64_t tok_end, int32_t channels,
+                           const int64_t *cu, int32_t n_segments, float eps, void *stream, h3_plan_info *info) {
+    if (mode != H3_ADALN_MODULATE && mode != H3_ADALN_GATE_RESIDUAL) {
+        clear_info(info);
+        return fail(H3_ERR_ARG, "mode = %d; legal values are %d (modulate) and %d (gate residual)", mode,
+                    H3_ADALN_MODULATE, H3_ADALN_GATE_RESIDUAL);
+    }
+    return adaln_impl(mode, x, branch, shift, scale, gate, nullptr, y, tok_begin, tok_end, channels, cu, n_segments,
+                      eps, stream, info);
+}
+
+h3_status h3_adaln_gate_modulate(const void *x, const void *branch, const void *gate, const void *shift,
+                                 const void *scale, void *resid, void *y, int64_t tok_begin, int64_t tok_end,
+                                 int32_t channels, const int64_t *cu, int32_t n_segments, float eps, void *stream,
+                                 h3_plan_info *info) {
+    return adaln_impl(H3_ADALN_GATE_MODULATE, x, branch, shift, scale, gate, resid, y, tok_begin, tok_end, channels,
+                      cu, n_segments, eps, stream, info);
 }
 
 }  // extern "C"

@@ -54,6 +54,28 @@ hipError_t launch_head2seq(const RunCopyArgs &a, int n_ranks, uint32_t max_run, 
                            int *grid_x);
 
 // ---------------------------------------------------------------------------
+// Ragged collectives of the token-sharded blocks (reduce-scatter, row gather).
+// Grid row y serves rank slot y: its rows are the contiguous vectors
+// [row_vec0[y], row_vec0[y] + n_vec[y]) of every [N][C] buffer.
+// ---------------------------------------------------------------------------
+struct RaggedArgs {
+    const void *src[kMaxRanks];      // reduce-scatter: partial of rank j (all N rows); gather: shard of slot y
+    void *dst[kMaxRanks];            // reduce-scatter: output rows of slot y
+    void *dst_all;                   // gather: the [N][C] result
+    const void *bias;                // reduce-scatter: [C] or NULL
+    uint64_t row_vec0[kMaxRanks];    // a_i * C / 8 of slot y's rank
+    uint32_t n_vec[kMaxRanks];       // N_i * C / 8 of slot y's rank (< 2^31)
+    FastDiv div_row;                 // division by nv_row (nv_row >= 2)
+    uint32_t nv_row;                 // C / 8
+    int32_t world;                   // reduce-scatter: partials summed
+};
+
+constexpr int kRsVec = 4;            // reduce-scatter: 16-byte output vectors per thread
+
+hipError_t launch_reduce_scatter(const RaggedArgs &a, int n_slots, uint32_t max_vec, hipStream_t s, int *grid_x);
+hipError_t launch_gather_rows(const RaggedArgs &a, int n_slots, uint32_t max_vec, hipStream_t s, int *grid_x);
+
+// ---------------------------------------------------------------------------
 // AdaLN on one token interval, with the clipped and rebased segment table.
 // ---------------------------------------------------------------------------
 struct AdalnArgs {
@@ -63,6 +85,7 @@ struct AdalnArgs {
     const void *scale;
     const void *gate;
     void *y;
+    void *resid;                             // gated chain: the stored residual x + gate * b
     uint32_t n_rows;
     uint32_t channels;
     float eps;

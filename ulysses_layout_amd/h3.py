@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libh3.so")
 H3_OK = 0
 H3_ADALN_MODULATE = 0
 H3_ADALN_GATE_RESIDUAL = 1
+H3_ADALN_GATE_MODULATE = 2
 HEAD_DIM = 128
 STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3_ERR_SEGMENTS",
                 4: "H3_ERR_UNSUPPORTED", 5: "H3_ERR_ALIAS", 6: "H3_ERR_HIP"}
@@ -27,7 +28,7 @@ STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3
 # names every build of libh3.so must export (the declarations of include/h3.h)
 EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
            "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_packed_attn_backward_workspace",
-           "h3_adaln_segment", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
+           "h3_adaln_segment", "h3_adaln_gate_modulate", "h3_reduce_scatter", "h3_gather_rows", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
            "h3_version")
 
 
@@ -89,12 +90,15 @@ def _load() -> ctypes.CDLL:
     lib.h3_packed_attn_backward_workspace.argtypes = [i64, i32, i32]
     lib.h3_packed_attn_backward_workspace.restype = i64
     lib.h3_adaln_segment.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, i64p, i32, f32, vp, ip]
+    lib.h3_adaln_gate_modulate.argtypes = [vp] * 7 + [i64, i64, i32, i64p, i32, f32, vp, ip]
+    lib.h3_reduce_scatter.argtypes = [ctypes.POINTER(vp), vp, ctypes.POINTER(vp), i64, i32, i32, i32, vp, ip]
+    lib.h3_gather_rows.argtypes = [ctypes.POINTER(vp), vp, i64, i32, i32, vp, ip]
     lib.h3_partition.argtypes = [i64, i32, i32, i64p, i64p]
     lib.h3_clip_segments.argtypes = [i64p, i32, i64, i64, ctypes.POINTER(i32), i64p, i64p]
     lib.h3_clip_segments.restype = i32
     for name in ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward",
                  "h3_packed_attn", "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_adaln_segment",
-                 "h3_partition"):
+                 "h3_adaln_gate_modulate", "h3_reduce_scatter", "h3_gather_rows", "h3_partition"):
         getattr(lib, name).restype = ctypes.c_int
     lib.h3_status_string.argtypes = [ctypes.c_int]
     lib.h3_status_string.restype = ctypes.c_char_p
@@ -344,4 +348,56 @@ def adaln_segment(mode: int, x, branch, shift, scale, gate, y, tok_begin: int, t
     info = _PlanInfo()
     _check(_lib.h3_adaln_segment(int(mode), xp, bp, pp[0], pp[1], pp[2], yp, int(tok_begin), int(tok_end), c,
                                  cu, n_seg, float(eps), _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def adaln_gate_modulate(x, branch, gate, shift, scale, resid, y, tok_begin: int, tok_end: int,
+                        cu_seqlens: Sequence[int], eps: float = 1e-6, stream=None) -> PlanInfo:
+    """``resid = x + gate[s] * branch`` and ``y`` = its modulation by the next
+    sub-block's ``shift`` / ``scale``, on rows ``[tok_begin, tok_end)``; x,
+    branch, resid, y are [rows, C], parameters [S, C]."""
+    rows, c = x.shape
+    n_seg = len(cu_seqlens) - 1
+    xp, bp = _dev_bf16(x, "x", (rows, c)), _dev_bf16(branch, "branch", (rows, c))
+    rp, yp = _dev_bf16(resid, "resid", (rows, c)), _dev_bf16(y, "y", (rows, c))
+    gp, shp, scp = (_dev_bf16(t, nm, (n_seg, c)) for t, nm in ((gate, "gate"), (shift, "shift"), (scale, "scale")))
+    cu = _i64_array(cu_seqlens)
+    info = _PlanInfo()
+    _check(_lib.h3_adaln_gate_modulate(xp, bp, gp, shp, scp, rp, yp, int(tok_begin), int(tok_end), c, cu, n_seg,
+                                       float(eps), _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def reduce_scatter(partials: Sequence, bias, out: Sequence, rank: int = -1, stream=None) -> PlanInfo:
+    """Sum the P partials ``[N, C]``, add ``bias`` ``[C]`` (or None) once, and
+    write rank i's rows to ``out[i]`` ``[N_i, C]`` for the selected ranks
+    (``rank = -1``: all; other entries of ``out`` may be None)."""
+    world = len(partials)
+    n, c = partials[0].shape
+    pp = (ctypes.c_void_p * world)(*[_dev_bf16(t, f"partials[{j}]", (n, c)) for j, t in enumerate(partials)])
+    op = (ctypes.c_void_p * world)()
+    for i in range(world):
+        if rank in (-1, i):
+            op[i] = _dev_bf16(out[i], f"out[{i}]", (partition(n, world, i)[1], c))
+    bp = None if bias is None else _dev_bf16(bias, "bias", (c,))
+    info = _PlanInfo()
+    _check(_lib.h3_reduce_scatter(pp, bp, op, n, c, world, int(rank), _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def gather_rows(shards: Sequence, dst, stream=None) -> PlanInfo:
+    """Rank i's first N_i rows of ``shards[i]`` (``[>= N_i, C]``, e.g. one
+    padded block of a gathered buffer) to rows ``[a_i, a_i + N_i)`` of ``dst``
+    ``[N, C]``."""
+    world = len(shards)
+    n, c = dst.shape
+    dp = _dev_bf16(dst, "dst", (n, c))
+    sp = (ctypes.c_void_p * world)()
+    for i, t in enumerate(shards):
+        sp[i] = _dev_bf16(t, f"shards[{i}]")
+        if 1 <= world <= n and (t.dim() != 2 or t.shape[1] != c or t.shape[0] < partition(n, world, i)[1]):
+            raise ValueError(f"shards[{i}] has shape {tuple(t.shape)}; it needs at least "
+                             f"{partition(n, world, i)[1]} rows of {c} channels")
+    info = _PlanInfo()
+    _check(_lib.h3_gather_rows(sp, dp, n, c, world, _stream_ptr(stream), ctypes.byref(info)))
     return _info(info)
