@@ -19,12 +19,15 @@
 //                    buffered).  Waves 0-3 own dK and waves 4-7 own dV of the
 //                    32-key block w%4, so each holds one 64-register
 //                    accumulator (both would not fit beside the tiles' working
-//                    set); S is formed by both waves of a block.  Per 32-query
-//                    half of a tile, with the keys as MFMA columns (lane =
-//                    key): S = Q K^T and P from it with lse read per row from
-//                    LDS; the dV wave adds e^T P, the dK wave forms dP = e V^T
-//                    and dS = P (dP - D) and adds Q^T dS, the transposing LDS
-//                    load supplying e^T and Q^T.
+//                    set); the two waves of a block share a SIMD.  With the
+//                    keys as MFMA columns (lane = key), per tile: phase 1, the
+//                    dV wave forms S = Q K^T and P from it (lse read per row
+//                    from LDS) and hands P to the dK wave through LDS in bf16,
+//                    while the dK wave forms dP = e V^T; a barrier; phase 2,
+//                    the dV wave adds e^T P and the dK wave forms
+//                    dS = P (dP - D) and adds Q^T dS, the transposing LDS load
+//                    supplying e^T and Q^T.  Each SIMD issues the 4 products
+//                    of a block once, 16 MFMAs per wave.
 //   k_attn_bwd_dq    the forward's structure with the roles of the operands
 //                    reassigned: one workgroup per (segment, head, 256-query
 //                    tile), lane = query.  Per 64-key tile: S^T = K Q^T and
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     __shared__ __attribute__((aligned(16))) float sL1[kBN];
     __shared__ __attribute__((aligned(16))) float sD0[kBN];
     __shared__ __attribute__((aligned(16))) float sD1[kBN];
+    __shared__ __attribute__((aligned(16))) uint32_t sP[(kBwdKBlock / 32) * 2 * 64 * 8];
 
     const int lo = find_entry(a, blockIdx.x);
     const int seg_len = a.seg_len[lo];
@@ -281,85 +285,90 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
 
+    // P of the tile in bf16, handed from each dV wave to the dK wave of the same key block
+    // (kb = wave % 4 for both), in the register layout of both waves' MFMA results:
+    // [key block][query half][word quad][lane][4 words], 16 consecutive bytes per lane
+    uint32_t *const p_mine = sP + (kb * 4 * 64 + lane) * 4;
+
     auto compute_tile = [&](const uint16_t *tq, const uint16_t *te, const float *tl, const float *td) {
         // The LDS objects span more than the 64 KB a read's immediate offset reaches, so every
         // (object, offset) pair needs its own address register: the offsets are expanded here,
         // per tile, rather than kept live across the loop.
         int ro[kD / 16], to[kD / 32][2];
         expand_offsets(coff, ro, to);
+        // phase 1: the dV wave forms S = Q K^T and P (lane = key; register r holds query row
+        // qh*32 + 8*(r/4) + 4*half + r%4) and publishes P; the dK wave forms dP = e V^T
+        uint32_t pw[2][8];
+        f32x16 dp[2];
+        // each K (V) fragment of the wave's keys is read once and used for both 32-query halves
+        if (dv_wave) {
+            f32x16 sc[2] = {};
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {                 // the two 32-query halves of the tile
-            const int q_base = qh * 32 * kD;
-            // S = Q K^T, 32 queries x 32 keys, lane = key
-            f32x16 s = {};
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                const bf16x8 kf = lds_b128(sK + k_base + ro[ks]);
 #pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + q_base + ro[ks]),
-                                                            lds_b128(sK + k_base + ro[ks]), s, 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int qh = 0; qh < 2; ++qh)
+                    sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + qh * 32 * kD + ro[ks]), kf,
+                                                                     sc[qh], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (dv_wave) {
-                // P (register r holds query row qh*32 + 8*(r/4) + 4*half + r%4), then dV^T += e^T P
-                uint32_t pw[8];
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i + e], a.scale_log2, -lv[e]));
-                    pw[2 * i] = pack_bf16x2(p[0], p[1]);
-                    pw[2 * i + 1] = pack_bf16x2(p[2], p[3]);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {       // 16-query step j uses registers 8j..8j+7
-                    const bf16x8 pb =
-                        __builtin_bit_cast(bf16x8, (u32x4){pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
-#pragma unroll
-                    for (int db = 0; db < kD / 32; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            tr_frag(te + q_base + 16 * j * kD, to, db), pb, acc[db], 0, 0, 0);
-                }
-            } else {
-                // dP = e V^T, dS = P (dP - D), then dK^T += Q^T dS
-                f32x16 dp = {};
-#pragma unroll
-                for (int ks = 0; ks < kD / 16; ++ks)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + q_base + ro[ks]),
-                                                                 lds_b128(sV + k_base + ro[ks]), dp, 0, 0, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-                for (int i = 0; i < 6; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-                uint32_t dw[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
-                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
-                    float ds[4];
+                    float pr[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i + e], a.scale_log2, -lv[e])) *
-                                (dp[4 * i + e] - dv[e]);
-                    dw[2 * i] = pack_bf16x2(ds[0], ds[1]);
-                    dw[2 * i + 1] = pack_bf16x2(ds[2], ds[3]);
+                        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qh][4 * i + e], a.scale_log2, -lv[e]));
+                    pw[qh][2 * i] = pack_bf16x2(pr[0], pr[1]);
+                    pw[qh][2 * i + 1] = pack_bf16x2(pr[2], pr[3]);
                 }
+                *reinterpret_cast<u32x4 *>(p_mine + qh * 512) = (u32x4){pw[qh][0], pw[qh][1], pw[qh][2], pw[qh][3]};
+                *reinterpret_cast<u32x4 *>(p_mine + qh * 512 + 256) =
+                    (u32x4){pw[qh][4], pw[qh][5], pw[qh][6], pw[qh][7]};
+            }
+        } else {
+            dp[0] = (f32x16){};
+            dp[1] = (f32x16){};
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const bf16x8 dsb =
-                        __builtin_bit_cast(bf16x8, (u32x4){dw[4 * j], dw[4 * j + 1], dw[4 * j + 2], dw[4 * j + 3]});
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                const bf16x8 vf = lds_b128(sV + k_base + ro[ks]);
 #pragma unroll
-                    for (int db = 0; db < kD / 32; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            tr_frag(tq + q_base + 16 * j * kD, to, db), dsb, acc[db], 0, 0, 0);
+                for (int qh = 0; qh < 2; ++qh)
+                    dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + qh * 32 * kD + ro[ks]), vf,
+                                                                     dp[qh], 0, 0, 0);
+            }
+        }
+        __syncthreads();                                 // P of the whole tile is in LDS
+        // phase 2: dV^T += e^T P (dV wave); dS = P (dP - D), dK^T += Q^T dS (dK wave)
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+            const int q_base = qh * 32 * kD;
+            uint32_t w[8];
+            if (dv_wave) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = pw[qh][i];
+            } else {
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(p_mine + qh * 512);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(p_mine + qh * 512 + 256);
+                const uint32_t pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
+                    w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * (dp[qh][4 * i] - dv[0]),
+                                           bf16_hi(pr[2 * i]) * (dp[qh][4 * i + 1] - dv[1]));
+                    w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * (dp[qh][4 * i + 2] - dv[2]),
+                                               bf16_hi(pr[2 * i + 1]) * (dp[qh][4 * i + 3] - dv[3]));
                 }
+            }
+            const uint16_t *tt = dv_wave ? te : tq;      // e^T for dV, Q^T for dK
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {                // 16-query step j uses registers 8j..8j+7
+                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tt + q_base + 16 * j * kD, to, db), b,
+                                                                      acc[db], 0, 0, 0);
             }
         }
     };
