@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample (attention part)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-workloads", default="32k_p4,250k_p8_qkvg",
+                    help="workloads also timed after the main one (comma list, '' for none); reported under "
+                         "'workloads', never in value")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run a plain torch copy of this many MiB three times, so hardware byte "
                          "counters can be scaled against a transfer of known size")
@@ -101,32 +104,55 @@ def cpu_baseline(step, workload, budget_s: float):
     rng = np.random.default_rng(workload.seed)
     cu = step.cu
     seg_len = np.diff(np.asarray(cu))
-    done_rows, flops, spent = 0, 0.0, 0.0
+    done_rows, flops, spent, sampled = 0, 0.0, 0.0, []
     heads = q.shape[1]
     while spent < budget_s:
         rows = np.sort(rng.integers(0, step.n_tokens, size=16))
         t0 = time.perf_counter()
-        oracle.attention_rows(q, k, v, g, cu, step.scale, rows=rows, threads=threads)
+        res = oracle.attention_rows(q, k, v, g, cu, step.scale, rows=rows, threads=threads)
         spent += time.perf_counter() - t0
         seg_of = np.searchsorted(np.asarray(cu), rows, side="right") - 1
         flops += float(4 * 128 * heads * seg_len[seg_of].sum())
         done_rows += len(rows)
+        sampled.append((rows, res))
     # AdaLN modulation on the first 4096 rows of rank 0's interval
     xb = bits(step.x[:4096])
     prm = [bits(t) for t in (step.shift, step.ada_scale)]
     t0 = time.perf_counter()
-    oracle.adaln_rows(0, xb, None, prm[0], prm[1], None, 0, 4096, cu, step.eps, threads=threads)
+    ada_ref = oracle.adaln_rows(0, xb, None, prm[0], prm[1], None, 0, 4096, cu, step.eps, threads=threads)
     adaln_s = time.perf_counter() - t0
+    rate = flops / spent
+
+    # outside the timed parts: the GPU's outputs of the last step against the oracle on the same samples
+    def err(got_bits, ref):
+        e = oracle.bf16_bits_to_f64(got_bits) - ref
+        return {"max_abs": float(np.abs(e).max()), "rel_rms": float(np.linalg.norm(e) / np.linalg.norm(ref)),
+                "max_abs_ref": float(np.abs(ref).max())}
+
+    rows = np.concatenate([r for r, _ in sampled])
+    attn_ref = np.concatenate([x for _, x in sampled])
+    attn_err = err(bits(step.attn_out[j][torch.from_numpy(rows).cuda()]), attn_ref)
+    ada_err = err(bits(step.y[:4096]), ada_ref)
+    relayout_exact = all(np.array_equal(bits(step.rank_bufs[j][p]), bufs[(j, p)]) for p in range(step.planes))
+    parity = {"relayout_rank_buffers_bit_exact": relayout_exact,
+              "attention_sampled_rows": int(rows.size), "attention": attn_err,
+              "adaln_rows": 4096, "adaln": ada_err,
+              "within_bar": bool(relayout_exact and attn_err["max_abs"] <= 2e-2 and attn_err["rel_rms"] <= 5e-3
+                                 and ada_err["max_abs"] <= 2e-2 and ada_err["rel_rms"] <= 5e-3),
+              # a bf16 half-ulp passes the max-abs bar only below 8
+              "max_abs_ref_below_8": bool(attn_err["max_abs_ref"] < 8 and ada_err["max_abs_ref"] < 8)}
     return {
-        "value": flops / spent / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 attention of {done_rows} seeded random query rows x {heads} heads over their full "
-                   f"segments ({flops:.3e} FLOP in {spent:.1f} s); relayout: oracle seq2head of rank {j}'s "
-                   f"share, all {step.planes} planes; AdaLN: 4096 modulated rows"),
+                   f"segments ({flops:.3e} FLOP in {spent:.1f} s, {rate / 1e9:.1f} GFLOP/s); relayout: oracle "
+                   f"seq2head of rank {j}'s share, all {step.planes} planes; AdaLN: 4096 modulated rows"),
+        "full_attention_s_extrapolated": step.attention_flops() / rate,
         "relayout_GBps": relayout_bytes / relayout_s / 1e9,
         "adaln_GBps": 2 * xb.nbytes / adaln_s / 1e9,
+        "parity_of_this_run": parity,
     }
 
 
@@ -263,6 +289,78 @@ def measure_next(step, reps: int = 5) -> dict:
     return out
 
 
+def run_steps(step, steps: int, warmup: int):
+    """Warm up, then time ``steps`` whole passes with HIP events around each of
+    the four steps.  Returns (mean ms per step name, wall seconds)."""
+    import torch
+
+    names = ("seq2head", "attention", "head2seq", "adaln")
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    events = [{n: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for n in names}
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step.run(events=events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in events) / steps for n in names}
+    ms["attention_median"] = sorted(e["attention"][0].elapsed_time(e["attention"][1]) for e in events)[steps // 2]
+    return ms, wall
+
+
+def make_step(w):
+    import torch
+
+    from synth.inputs import normal_bf16
+    from ulysses_layout_amd.pipeline import UlyssesStep
+
+    attn_ranks = None if w.attn_rank is None else [w.attn_rank]
+    step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
+                       max_chunk_bytes=w.max_chunk_bytes)
+    step.qkv.copy_(normal_bf16(step.qkv.shape, seed=w.seed, device="cuda"))
+    step.x.copy_(normal_bf16(step.x.shape, seed=w.seed + 1, device="cuda"))
+    for i, t in enumerate((step.shift, step.ada_scale, step.gate)):
+        t.copy_(normal_bf16(t.shape, seed=w.seed + 3 + i, std=0.1, device="cuda"))
+    torch.cuda.synchronize()
+    return step
+
+
+def step_rates(step, ms) -> dict:
+    rb = step.relayout_bytes()
+    attn_tflops = step.attention_flops() / (ms["attention"] * 1e-3) / 1e12
+    rel_gbps = (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3) / 1e9
+    ada_gbps = step.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9
+    return {"attention_TFLOPs": attn_tflops, "attention_frac_bf16": attn_tflops / PEAK_BF16_TFLOPS,
+            "relayout_GBps": rel_gbps, "relayout_frac_hbm": rel_gbps / PEAK_HBM_GBPS,
+            "adaln_GBps": ada_gbps, "adaln_frac_hbm": ada_gbps / PEAK_HBM_GBPS,
+            "ms": ms}
+
+
+def measure_workloads(names, steps: int = 3, warmup: int = 1) -> dict:
+    """The same pass at the other workloads, one after another, each freed
+    before the next; reported beside the main line."""
+    import torch
+
+    from synth import WORKLOADS
+
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        step = make_step(w)
+        ms, _ = run_steps(step, steps, warmup)
+        r = step_rates(step, ms)
+        r.update({"n_tokens": w.n_tokens, "segments": len(w.cu) - 1, "virtual_ranks": w.world,
+                  "attention_heads": sum(step.heads[j][1] for j in step.attn_ranks), "planes": w.planes,
+                  "steps": steps})
+        out[name] = r
+        del step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -273,8 +371,6 @@ def main():
     import torch
 
     from synth import WORKLOADS
-    from synth.inputs import normal_bf16
-    from ulysses_layout_amd.pipeline import UlyssesStep
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -289,28 +385,8 @@ def main():
         print(f"calibration copy: {n} bytes read and {n} bytes written per launch, 3 launches", file=sys.stderr)
         del a, b
     w = WORKLOADS[args.workload]
-    attn_ranks = None if w.attn_rank is None else [w.attn_rank]
-    step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
-                       max_chunk_bytes=w.max_chunk_bytes)
-    step.qkv.copy_(normal_bf16(step.qkv.shape, seed=w.seed, device="cuda"))
-    step.x.copy_(normal_bf16(step.x.shape, seed=w.seed + 1, device="cuda"))
-    for i, t in enumerate((step.shift, step.ada_scale, step.gate)):
-        t.copy_(normal_bf16(t.shape, seed=w.seed + 3 + i, std=0.1, device="cuda"))
-    torch.cuda.synchronize()
-
-    names = ("seq2head", "attention", "head2seq", "adaln")
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-    events = [{n: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for n in names}
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step.run(events=events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in events) / args.steps for n in names}
+    step = make_step(w)
+    ms, wall = run_steps(step, args.steps, args.warmup)
 
     attn_flops = step.attention_flops()
     rb = step.relayout_bytes()
@@ -324,12 +400,14 @@ def main():
     traffic = read_traffic(flops_per_launch)
     backward = measure_backward(step)
     next_ops = measure_next(step)
+    workloads = measure_workloads([n for n in args.other_workloads.split(",") if n and n != w.name])
 
     components = {
         "seq2head": {"ms": ms["seq2head"], "GBps": s2h_gbps, "frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
                      "bytes": rb["seq2head"], "launches": sum(p.launches for p in step.last_plans["seq2head"])},
         "attention": {"ms": ms["attention"], "TFLOPs": attn_tflops, "frac_bf16": attn_tflops / PEAK_BF16_TFLOPS,
-                      "flops": attn_flops, "launches": attn_launches},
+                      "flops": attn_flops, "launches": attn_launches, "ms_median": ms["attention_median"],
+                      "TFLOPs_median": attn_flops / (ms["attention_median"] * 1e-3) / 1e12},
         "head2seq": {"ms": ms["head2seq"], "GBps": h2s_gbps, "frac_hbm": h2s_gbps / PEAK_HBM_GBPS,
                      "bytes": rb["head2seq"]},
         "adaln": {"ms": ms["adaln"], "GBps": ada_gbps, "frac_hbm": ada_gbps / PEAK_HBM_GBPS,
@@ -368,6 +446,7 @@ def main():
         "components": components,
         "backward": backward,
         "token_sharded_ops": next_ops,
+        "workloads": workloads,
         "roofline": {
             "kernel": ATTN_KERNEL,
             "bound": "mfma",
