@@ -267,13 +267,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + lds_row * kD), 16, off, 0, 0, 0);
         }
     };
-    // lse (base 2, +inf past the segment end) and D of a query tile: wave 0 and wave 1, one value per lane
+    // lse (base 2, +inf past the segment end) and -D of a query tile: wave 0 and wave 1, one value per lane
+    // (-D seeds the dP accumulator, so the MFMA chain yields dP - D)
     auto row_value = [&](int qt) -> float {
         const int qrow = qt * kBN + lane;
         if (wave == 0) {
             return qrow < seg_len ? a.lse[(seg_row0 + qrow) * a.n_heads + head] * kLog2e : __builtin_inff();
         }
-        return qrow < seg_len ? a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
+        return qrow < seg_len ? -a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
     };
 
     // per-lane LDS offsets: row l32 of a 32-row block, chunk 2ks+half (f(row) repeats every 16 rows,
@@ -328,8 +329,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
                     (u32x4){pw[qh][4], pw[qh][5], pw[qh][6], pw[qh][7]};
             }
         } else {
-            dp[0] = (f32x16){};
-            dp[1] = (f32x16){};
+            // dP - D: the accumulator starts from -D of each register's query row
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 nd = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dp[qh][4 * i + e] = nd[e];
+                }
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
                 const bf16x8 vf = lds_b128(sV + k_base + ro[ks]);
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             }
         }
         __syncthreads();                                 // P of the whole tile is in LDS
-        // phase 2: dV^T += e^T P (dV wave); dS = P (dP - D), dK^T += Q^T dS (dK wave)
+        // phase 2: dV^T += e^T P (dV wave); dS = P (dP - D), dK^T += Q^T dS (dK wave; dp holds dP - D)
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
             const int q_base = qh * 32 * kD;
@@ -354,11 +362,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
                 const uint32_t pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
-                    w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * (dp[qh][4 * i] - dv[0]),
-                                           bf16_hi(pr[2 * i]) * (dp[qh][4 * i + 1] - dv[1]));
-                    w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * (dp[qh][4 * i + 2] - dv[2]),
-                                               bf16_hi(pr[2 * i + 1]) * (dp[qh][4 * i + 3] - dv[3]));
+                    w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * dp[qh][4 * i], bf16_hi(pr[2 * i]) * dp[qh][4 * i + 1]);
+                    w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * dp[qh][4 * i + 2],
+                                               bf16_hi(pr[2 * i + 1]) * dp[qh][4 * i + 3]);
                 }
             }
             const uint16_t *tt = dv_wave ? te : tq;      // e^T for dV, Q^T for dK
