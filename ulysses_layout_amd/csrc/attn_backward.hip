@@ -588,7 +588,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
 }
 
 hipError_t launch_attn_bwd_pre(const AttnBwdArgs &a, hipStream_t s, int *grid_x) {
-    const uint32_t gx = (a.n_rows + kBwdPreRowsPerWg - 1) / kBwdPreRowsPerWg;
+    const uint32_t gx = (uint32_t)(((uint64_t)a.n_rows + kBwdPreRowsPerWg - 1) / kBwdPreRowsPerWg);
     if (grid_x) *grid_x = (int)gx;
     if (gx == 0) return hipSuccess;
     hipLaunchKernelGGL(k_attn_bwd_pre, dim3(gx), dim3(256), 0, s, a);
