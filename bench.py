@@ -156,78 +156,48 @@ def cpu_baseline(step, workload, budget_s: float):
     }
 
 
-def measure_backward(step, reps: int = 5) -> dict:
-    """The backward of the path at the same workload and plan, timed with HIP
-    events after the timed steps: the relayout adjoints (backward of seq2head
-    and head2seq) and the attention backward of one attended rank's heads.
-    They are reported beside the step, not folded into ``value``."""
+def measure_backward(w, reps: int = 5) -> dict:
+    """The path's backward at the same workload and plan, on a step built with
+    backward buffers (its attention also stores the row log-sum-exp): after one
+    forward pass, ``UlyssesStep.backward()`` -- head2seq adjoint, attention
+    backward of the attended rank(s), seq2head adjoint -- timed with HIP events
+    per phase over ``reps`` passes.  Reported beside the step, not in ``value``."""
     import torch
 
-    import ulysses_layout_amd as h3
-
-    grad_src = torch.empty_like(step.qkv)                 # [N, K, H, D] gradient of the packed operand
-    st = torch.cuda.current_stream()
-
-    def s2h_bwd():
-        return h3.seq2head_backward(step.rank_bufs, grad_src, step.world, rank=step.relayout_rank,
-                                    max_chunk_bytes=step.max_chunk_bytes, stream=st)
-
-    def h2s_bwd():
-        return h3.head2seq_backward(step.out, step.attn_out, step.world, rank=step.head2seq_rank,
-                                    max_chunk_bytes=step.max_chunk_bytes, stream=st)
-
-    rb = step.relayout_bytes()
-    out = {}
-    for name, fn, nbytes in (("seq2head_backward", s2h_bwd, rb["seq2head"]), ("head2seq_backward", h2s_bwd,
-                                                                                rb["head2seq"])):
-        fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        plan = None
-        for a, b in ev:
-            a.record(st)
-            plan = fn()
-            b.record(st)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": ms, "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes,
-                     "launches": plan.launches}
-    del grad_src
-
-    # attention backward for the first attended rank: forward with the row
-    # log-sum-exp, then dq, dk, dv (dg) from a seeded upstream gradient
     from synth.inputs import normal_bf16
-    j = step.attn_ranks[0]
-    b = step.rank_bufs[j]
-    g = b[3] if step.gated else None
-    o = step.attn_out[j]
-    n, h, _ = o.shape
-    lse = torch.empty((n, h), dtype=torch.float32, device="cuda")
-    h3.packed_attn(b[0], b[1], b[2], g, o, step.cu, step.scale, lse=lse, stream=st)
-    dout = normal_bf16(o.shape, seed=4242, device="cuda")
-    grads = [torch.empty_like(o) for _ in range(4 if step.gated else 3)]
-    ws = torch.empty(h3.packed_attn_backward_workspace(n, h, step.gated), dtype=torch.uint8, device="cuda")
 
-    def attn_bwd():
-        return h3.packed_attn_backward(b[0], b[1], b[2], g, o, dout, lse, grads[0], grads[1], grads[2],
-                                       grads[3] if step.gated else None, ws, step.cu, step.scale, stream=st)
-
-    attn_bwd()
+    step = make_step(w, with_backward=True)
+    step.grad_out.copy_(normal_bf16(step.grad_out.shape, seed=4242, device="cuda"))
+    step.run()
+    step.backward()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    info = None
-    for a, e in ev:
-        a.record(st)
-        info = attn_bwd()
-        e.record(st)
+    names = ("head2seq_backward", "attention_backward", "seq2head_backward")
+    events = [{n: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for n in names}
+              for _ in range(reps)]
+    plans = None
+    for i in range(reps):
+        plans = step.backward(events=events[i])
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(e) for a, e in ev) / reps
-    tflops = info.flops / (ms * 1e-3) / 1e12
-    out["attention_backward"] = {"ms": ms, "TFLOPs": tflops, "frac_bf16": tflops / PEAK_BF16_TFLOPS,
-                                 "flops": info.flops, "launches": info.launches, "heads": h, "gated": step.gated,
+    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in events) / reps for n in names}
+    h2s_bytes = 2 * w.n_tokens * sum(step.heads[j][1] for j in step.attn_ranks) * 128 * 2
+    s2h_bytes = step.planes * h2s_bytes
+    flops = sum(p.flops for p in plans["attention_backward"])
+    out = {}
+    for name, nbytes in (("head2seq_backward", h2s_bytes), ("seq2head_backward", s2h_bytes)):
+        gbps = nbytes / (ms[name] * 1e-3) / 1e9
+        out[name] = {"ms": ms[name], "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes,
+                     "launches": sum(p.launches for p in plans[name])}
+    tflops = flops / (ms["attention_backward"] * 1e-3) / 1e12
+    out["attention_backward"] = {"ms": ms["attention_backward"], "TFLOPs": tflops,
+                                 "frac_bf16": tflops / PEAK_BF16_TFLOPS, "flops": flops,
+                                 "launches": sum(p.launches for p in plans["attention_backward"]),
+                                 "heads": sum(step.heads[j][1] for j in step.attn_ranks), "gated": step.gated,
                                  "flops_rule": "10 * head_dim per (query, key) pair per head"}
-    del grads, ws, dout, lse
+    out["step_ms"] = sum(ms.values())
+    out["what"] = ("UlyssesStep.backward(): gradient of the head2seq output -> attention backward (row lse "
+                   "stored by the forward) -> gradient of the packed operand, attended rank(s) only")
+    del step
+    torch.cuda.empty_cache()
     return out
 
 
@@ -311,7 +281,7 @@ def run_steps(step, steps: int, warmup: int):
     return ms, wall
 
 
-def make_step(w):
+def make_step(w, with_backward: bool = False):
     import torch
 
     from synth.inputs import normal_bf16
@@ -319,7 +289,7 @@ def make_step(w):
 
     attn_ranks = None if w.attn_rank is None else [w.attn_rank]
     step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
-                       max_chunk_bytes=w.max_chunk_bytes)
+                       max_chunk_bytes=w.max_chunk_bytes, with_backward=with_backward)
     step.qkv.copy_(normal_bf16(step.qkv.shape, seed=w.seed, device="cuda"))
     step.x.copy_(normal_bf16(step.x.shape, seed=w.seed + 1, device="cuda"))
     for i, t in enumerate((step.shift, step.ada_scale, step.gate)):
@@ -398,7 +368,7 @@ def main():
     flops_per_launch = attn_flops / attn_launches
     launch_ms = ms["attention"] / attn_launches
     traffic = read_traffic(flops_per_launch)
-    backward = measure_backward(step)
+    backward = measure_backward(w)
     next_ops = measure_next(step)
     workloads = measure_workloads([n for n in args.other_workloads.split(",") if n and n != w.name])
 

@@ -12,8 +12,13 @@ stream, the four library calls in the order the Ulysses block runs them
 4. ``h3_adaln_segment`` per virtual rank's token interval, with the segment
                      table clipped and rebased to it, on ``[N_j, 7168]`` rows.
 
-It allocates nothing inside ``run()``; buffers are made once by the
-constructor.  All arithmetic happens in libh3.so.
+With ``with_backward=True`` the attention also stores each row's
+log-sum-exp, and ``backward()`` enqueues the path's backward in reverse
+order: ``h3_head2seq_backward`` of ``grad_out``, ``h3_packed_attn_backward``
+for each attended rank, and ``h3_seq2head_backward`` into ``grad_qkv``.
+
+It allocates nothing inside ``run()`` or ``backward()``; buffers are made once
+by the constructor.  All arithmetic happens in libh3.so.
 """
 from __future__ import annotations
 
@@ -46,7 +51,7 @@ class UlyssesStep:
                  attn_ranks: Optional[Sequence[int]] = None, relayout_rank: int = -1,
                  max_chunk_bytes: int = 0, n_heads: int = H3_HEADS, channels: Optional[int] = None,
                  scale: float = _h3.HEAD_DIM ** -0.5, eps: float = 1e-6, adaln_modes=("modulate",),
-                 device: str = "cuda"):
+                 with_backward: bool = False, device: str = "cuda"):
         self.n_tokens = int(n_tokens)
         self.cu = [int(c) for c in cu]
         self.world = int(world)
@@ -92,6 +97,24 @@ class UlyssesStep:
         if self.head2seq_rank is None:
             raise ValueError("attention must cover one rank or every rank")
         self.last_plans: Dict[str, List[_h3.PlanInfo]] = {}
+        # backward buffers: the caller fills grad_out (the gradient of `out`)
+        self.with_backward = bool(with_backward)
+        self.lse: List[Optional[torch.Tensor]] = [None] * self.world
+        if self.with_backward:
+            f32 = torch.float32
+            self.grad_out = torch.empty((n, self.n_heads, d), dtype=bf, device=dev)
+            self.grad_attn: List[Optional[torch.Tensor]] = [None] * self.world
+            self.grad_bufs: List[Optional[List[torch.Tensor]]] = [None] * self.world
+            self.workspace: List[Optional[torch.Tensor]] = [None] * self.world
+            for j in self.attn_ranks:
+                hj = self.heads[j][1]
+                self.lse[j] = torch.empty((n, hj), dtype=f32, device=dev)
+                self.grad_attn[j] = torch.empty((n, hj, d), dtype=bf, device=dev)
+                self.grad_bufs[j] = [torch.empty((n, hj, d), dtype=bf, device=dev) for _ in range(self.planes)]
+                self.workspace[j] = torch.empty(_h3.packed_attn_backward_workspace(n, hj, self.gated),
+                                                dtype=torch.uint8, device=dev)
+            # heads outside the attended ranks receive no gradient and stay zero
+            self.grad_qkv = torch.zeros((n, self.planes, self.n_heads, d), dtype=bf, device=dev)
 
     # -- the four steps -------------------------------------------------------------
     def seq2head(self, stream=None) -> _h3.PlanInfo:
@@ -103,7 +126,7 @@ class UlyssesStep:
         for j in self.attn_ranks:
             b = self.rank_bufs[j]
             plans.append(_h3.packed_attn(b[0], b[1], b[2], b[3] if self.gated else None, self.attn_out[j],
-                                         self.cu, self.scale, stream=stream))
+                                         self.cu, self.scale, stream=stream, lse=self.lse[j]))
         return plans
 
     def head2seq(self, stream=None) -> _h3.PlanInfo:
@@ -136,6 +159,44 @@ class UlyssesStep:
             self.last_plans[name] = plan if isinstance(plan, list) else [plan]
             if events is not None:
                 events[name][1].record(st)
+
+    # -- the backward of the relayouts and the attention --------------------------------
+    def backward(self, stream=None, events: Optional[Dict[str, List]] = None) -> Dict[str, List[_h3.PlanInfo]]:
+        """Gradients of the packed operand from ``grad_out`` (after a ``run``):
+        head2seq adjoint, attention backward per attended rank, seq2head
+        adjoint (of the attended ranks' heads, with the forward's chunking)."""
+        if not self.with_backward:
+            raise RuntimeError("construct the step with with_backward=True")
+        st = stream if stream is not None else torch.cuda.current_stream()
+        plans: Dict[str, List[_h3.PlanInfo]] = {}
+
+        def timed(name, fn):
+            if events is not None:
+                events[name][0].record(st)
+            res = fn()
+            if events is not None:
+                events[name][1].record(st)
+            plans[name] = res if isinstance(res, list) else [res]
+
+        timed("head2seq_backward", lambda: _h3.head2seq_backward(
+            self.grad_out, self.grad_attn, self.world, rank=self.head2seq_rank,
+            max_chunk_bytes=self.max_chunk_bytes, stream=st))
+
+        def attn_bwd():
+            out = []
+            for j in self.attn_ranks:
+                b, gb = self.rank_bufs[j], self.grad_bufs[j]
+                out.append(_h3.packed_attn_backward(
+                    b[0], b[1], b[2], b[3] if self.gated else None, self.attn_out[j], self.grad_attn[j],
+                    self.lse[j], gb[0], gb[1], gb[2], gb[3] if self.gated else None, self.workspace[j], self.cu,
+                    self.scale, stream=st))
+            return out
+
+        timed("attention_backward", attn_bwd)
+        timed("seq2head_backward", lambda: _h3.seq2head_backward(
+            self.grad_bufs, self.grad_qkv, self.world, rank=self.head2seq_rank,
+            max_chunk_bytes=self.max_chunk_bytes, stream=st))
+        return plans
 
     # -- algorithmic work of one pass ------------------------------------------------
     def attention_flops(self) -> float:
