@@ -385,26 +385,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
         const float rv = row_value(0);
         (wave == 0 ? sL0 : sD0)[lane] = rv;
     }
-    // ---- main loop over query tiles, two per trip so buffer addresses are constants -
-    for (int qt = 0; qt < n_qt; qt += 2) {
+    // ---- main loop over query tiles; the double buffers alternate by tile parity (one
+    // instance of the tile body: unrolled by two, the register allocator moved the
+    // accumulators to a second register range every other tile)
+    for (int qt = 0; qt < n_qt; ++qt) {
+        const bool odd = (qt & 1) != 0;
         __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): this lane's loads of tile qt landed
         __syncthreads();
         float nv = 0.f;
         if (qt + 1 < n_qt) {
-            issue_tile(qt + 1, sQ1, sE1);
+            issue_tile(qt + 1, odd ? sQ0 : sQ1, odd ? sE0 : sE1);
             if (wave < 2) nv = row_value(qt + 1);
         }
-        compute_tile(sQ0, sE0, sL0, sD0);
-        if (qt + 1 < n_qt && wave < 2) (wave == 0 ? sL1 : sD1)[lane] = nv;
-        if (qt + 1 >= n_qt) break;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (qt + 2 < n_qt) {
-            issue_tile(qt + 2, sQ0, sE0);
-            if (wave < 2) nv = row_value(qt + 2);
-        }
-        compute_tile(sQ1, sE1, sL1, sD1);
-        if (qt + 2 < n_qt && wave < 2) (wave == 0 ? sL0 : sD0)[lane] = nv;
+        compute_tile(odd ? sQ1 : sQ0, odd ? sE1 : sE0, odd ? sL1 : sL0, odd ? sD1 : sD0);
+        if (qt + 1 < n_qt && wave < 2) (wave == 0 ? (odd ? sL0 : sL1) : (odd ? sD0 : sD1))[lane] = nv;
     }
 
     // ---- store this wave's 32 keys: lane = key, register r = channel db*32 + 8*(r/4) + 4*half + r%4
@@ -562,16 +556,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     };
 
     issue_tile(0, sK0, sV0);
-    for (int kt = 0; kt < n_kt; kt += 2) {
+    // one instance of the tile body, buffers alternating by tile parity (as in the dk/dv kernel)
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const bool odd = (kt & 1) != 0;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (kt + 1 < n_kt) issue_tile(kt + 1, sK1, sV1);
-        compute_tile(kt, sK0, sV0);
-        if (kt + 1 >= n_kt) break;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (kt + 2 < n_kt) issue_tile(kt + 2, sK0, sV0);
-        compute_tile(kt + 1, sK1, sV1);
+        if (kt + 1 < n_kt) issue_tile(kt + 1, odd ? sK0 : sK1, odd ? sV0 : sV1);
+        compute_tile(kt, odd ? sK1 : sK0, odd ? sV1 : sV0);
     }
 
     if (!q_valid) return;
