@@ -6,8 +6,12 @@
  * of packed QKV/QKVG, segment-masked attention over the natively packed
  * multi-segment sequence, the inverse head-to-sequence relayout, and the
  * per-segment AdaLN modulation / residual gating on segment tables clipped to
- * a token interval.  The P ranks of the sequence-parallel group are emulated
- * by P "virtual-rank" buffers on the one device; no collective is issued.
+ * a token interval.  Beside that forward path it provides the backward of
+ * the relayouts and of the attention, the gated AdaLN chain (one sub-block's
+ * residual gating fused with the next one's modulation), and the ragged
+ * reduce-scatter and row gather of the token-sharded blocks.  The P ranks of
+ * the sequence-parallel group are emulated by P "virtual-rank" buffers on the
+ * one device; no collective is issued.
  *
  * Sources (by page title and section):
  *   [DIST]  "Distributed H3 Execution" -- introduction, Partition Contract,
@@ -19,10 +23,13 @@
  *
  * Conventions common to every entry point
  * ---------------------------------------
- * - Element type: every tensor is bfloat16, row-major, densely packed.
+ * - Element type: every tensor is bfloat16, row-major, densely packed, except
+ *   the attention's row log-sum-exp (fp32) and the backward's workspace
+ *   (raw bytes).
  * - Pointers: "device" pointers are HIP device memory owned by the caller;
  *   "host" pointers are ordinary host memory read only during the call.
- *   The library never allocates, frees or synchronises; work is enqueued on
+ *   The library never allocates, frees or synchronises (scratch space, where
+ *   a kernel needs it, is a caller-owned workspace); work is enqueued on
  *   `stream` (a hipStream_t passed as void*, NULL = the default stream) and
  *   runs asynchronously.  Buffers must stay alive until that work completes.
  * - Independent storage ([PR], Problem and behavior): no output may overlap
