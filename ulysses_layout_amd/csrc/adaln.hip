@@ -15,23 +15,9 @@
 // row once.  Other multiples of 8 take a generic path that re-reads the row.
 // The segment of a row comes from the clipped table in the kernel arguments
 // by a wave-uniform binary search.
-#include "h3_internal.h"
+#include "h3_device.h"
 
 namespace h3 {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Round two floats to bf16 (nearest even) and pack them, element 0 in the low half.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2 f = {lo, hi};
-    bf16x2 b = __builtin_convertvector(f, bf16x2);
-    return __builtin_bit_cast(uint32_t, b);
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

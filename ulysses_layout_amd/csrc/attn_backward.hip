@@ -38,55 +38,25 @@
 // are masked to -inf (dq kernel), queries there get lse = +inf so their p is 0
 // (dk/dv kernel), and no output row past the end is written.
 //
-// MFMA layouts (v_mfma_f32_32x32x16_bf16), LDS swizzle and the transposing
-// read follow packed_attn.hip; see the comments there.
-#include "h3_internal.h"
+// MFMA layouts (v_mfma_f32_32x32x16_bf16) follow packed_attn.hip; the LDS
+// swizzle and the transposing read are those of h3_device.h.
+#include "h3_device.h"
 
 namespace h3 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 namespace {
 
-constexpr int kD = H3_HEAD_DIM;          // 128
 constexpr int kBN = 64;                  // keys per tile (dq) / queries per tile (dk/dv)
 constexpr int kTileElems = kBN * kD;
 constexpr int kWaves = kBwdThreads / 64; // 8
 constexpr int kLoadsPerTile = kBN / (4 * kWaves);          // 16-byte loads per lane per 64-row tile
 constexpr int kLoadsPerKBlock = kBwdKBlock / (4 * kWaves); // per 128-row key block
-constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdQBlock == 32 * kWaves, "one 32-query block per wave");
 static_assert(kBwdKBlock == 32 * (kWaves / 2), "a dK wave and a dV wave per 32-key block");
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2 f = {lo, hi};
-    bf16x2 b = __builtin_convertvector(f, bf16x2);
-    return __builtin_bit_cast(uint32_t, b);
-}
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
 
-// 16-byte chunk c of tile row r sits at chunk c ^ f(r) (as in packed_attn.hip)
-__device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r)) << 3); }
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_void *)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
@@ -512,13 +482,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tv + kb * 32 * kD + k_off[ks]), ereg[ks], dp, 0, 0,
                                                              0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
             for (int i = 0; i < 12; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
             if ((kt + 1) * kBN > seg_len) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -545,13 +515,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
                 for (int j = 0; j < 2; ++j)
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         tr_frag(tk + (kb * 32 + 16 * j) * kD, t_off, db), dsb[j], acc[db], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
             for (int i = 0; i < 6; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
         }
     };
 

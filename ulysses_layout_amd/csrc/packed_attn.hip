@@ -55,63 +55,18 @@
 // the swizzle is applied on the global side: lane l of a load fetches logical
 // chunk (l%16) ^ f(row).  Rows past the end of the segment are clamped to
 // its last row (finite data, masked out or weighted by 0).
-#include "h3_internal.h"
+#include "h3_device.h"
 
 namespace h3 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kD = H3_HEAD_DIM;          // 128
 constexpr int kBN = 64;                  // keys per tile
 constexpr int kTileElems = kBN * kD;     // one K or V tile
 constexpr int kWaves = kAttnThreads / 64;
 constexpr int kLoadsPerTile = kBN / (4 * kWaves);   // 16-byte direct loads per lane per operand
 constexpr float kLazyRescale = 8.0f;     // log2 of the largest tolerated probability
 constexpr float kMaxCheck = 128.0f;      // partial row sum that triggers the exact max (2^7 < 2^8)
-constexpr int kBufferWord3 = 0x00020000; // buffer resource word 3 for raw 32-bit data on gfx9-class parts
-constexpr int kSchedMfma = 0x008;        // sched_group_barrier class masks
-constexpr int kSchedDsRead = 0x100;
 static_assert(kAttnBlockM == 32 * kWaves, "one 32-query block per wave");
 static_assert(kLoadsPerTile * 4 * kWaves == kBN, "loads cover the tile");
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2 f = {lo, hi};
-    bf16x2 b = __builtin_convertvector(f, bf16x2);
-    return __builtin_bit_cast(uint32_t, b);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// element offset of (row r, 16-byte chunk c) inside a swizzled tile
-__device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r)) << 3); }
-
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// reductions across the two 32-lane halves (lane l and lane l ^ 32)
-__device__ __forceinline__ float half_max(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_void *)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
 
 __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     // Four distinct LDS objects (not one array of buffers) so the compiler can

@@ -18,23 +18,11 @@
 //   k_gather_rows     dst[a_i C/8 + f] = shard_i[f]: the rank's rows land at
 //                     their global position, so any padding after a shard's
 //                     N_i rows is never read.
-#include "h3_internal.h"
+#include "h3_device.h"
 
 namespace h3 {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 namespace {
-
-__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2 f = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-}
 
 // f mod nv for f < 2^31 (nv == 1 needs no division)
 __device__ __forceinline__ uint32_t vec_channel(uint32_t f, const RaggedArgs &a) {
@@ -47,8 +35,8 @@ __device__ __forceinline__ uint32_t vec_channel(uint32_t f, const RaggedArgs &a)
 __device__ __forceinline__ void add_vec(float (&acc)[8], u32x4 v) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        acc[2 * w] += lo16(v[w]);
-        acc[2 * w + 1] += hi16(v[w]);
+        acc[2 * w] += bf16_lo(v[w]);
+        acc[2 * w + 1] += bf16_hi(v[w]);
     }
 }
 
@@ -58,7 +46,7 @@ __device__ __forceinline__ u32x4 finish_vec(const float (&acc)[8], const u32x4 *
     if (bias) {
         const u32x4 bv = bias[vec_channel(f, a)];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) out[w] = pack_bf16x2(acc[2 * w] + lo16(bv[w]), acc[2 * w + 1] + hi16(bv[w]));
+        for (int w = 0; w < 4; ++w) out[w] = pack_bf16x2(acc[2 * w] + bf16_lo(bv[w]), acc[2 * w + 1] + bf16_hi(bv[w]));
     } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) out[w] = pack_bf16x2(acc[2 * w], acc[2 * w + 1]);

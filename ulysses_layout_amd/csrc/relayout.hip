@@ -13,11 +13,9 @@
 // before its stores, and both streams use non-temporal hints because every
 // byte is read once and written once.  No LDS staging is needed: the smallest
 // contiguous piece is a 256-byte row, four times the 64-byte HBM access unit.
-#include "h3_internal.h"
+#include "h3_device.h"
 
 namespace h3 {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t fast_udiv(uint32_t n, FastDiv f) {
     uint32_t q = __umulhi(n, f.m);
