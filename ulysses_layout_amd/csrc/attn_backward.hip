@@ -13,21 +13,22 @@
 //
 // Three launches:
 //   k_attn_bwd_pre   one 16-lane group per (token, head) row: e, dg and D.
-//   k_attn_bwd_dkdv  one workgroup per (segment, head, 128-key block).  The
-//                    block's K and V stay in LDS; 64-query tiles of Q and e
-//                    stream through LDS (buffer loads to LDS, double
-//                    buffered).  Waves 0-3 own dK and waves 4-7 own dV of the
-//                    32-key block w%4, so each holds one 64-register
-//                    accumulator (both would not fit beside the tiles' working
-//                    set); the two waves of a block share a SIMD.  With the
-//                    keys as MFMA columns (lane = key), per tile: phase 1, the
-//                    dV wave forms S = Q K^T and P from it (lse read per row
-//                    from LDS) and hands P to the dK wave through LDS in bf16,
-//                    while the dK wave forms dP = e V^T; a barrier; phase 2,
-//                    the dV wave adds e^T P and the dK wave forms
-//                    dS = P (dP - D) and adds Q^T dS, the transposing LDS load
-//                    supplying e^T and Q^T.  Each SIMD issues the 4 products
-//                    of a block once, 16 MFMAs per wave.
+//   k_attn_bwd_dkdv  one workgroup per (segment, head, 128-key block).
+//                    Waves 0-3 own dK and waves 4-7 own dV of the 32-key
+//                    block w%4 (one 64-register accumulator each; the two
+//                    waves of a block share a SIMD).  The block's K and V
+//                    pass once through LDS into registers (each wave keeps
+//                    the operand it multiplies by: K for the dV wave, V for
+//                    the dK wave).  64-query tiles of Q and e stream through
+//                    LDS (buffer loads to LDS; Q triple, e double buffered),
+//                    one barrier per tile.  With the keys as MFMA columns
+//                    (lane = key), in tile t the dV wave forms S = Q K^T and
+//                    P from it (lse per row from LDS), publishes P in bf16
+//                    through LDS and adds e^T P; the dK wave forms
+//                    dS = P (dP - D) of tile t-1 from the P published then
+//                    and the dP - D it carried over the barrier, adds Q^T dS,
+//                    and forms dP - D of tile t (the accumulator seeded with
+//                    -D).  The transposing LDS load supplies e^T and Q^T.
 //   k_attn_bwd_dq    the forward's structure with the roles of the operands
 //                    reassigned: one workgroup per (segment, head, 256-query
 //                    tile), lane = query.  Per 64-key tile: S^T = K Q^T and
@@ -158,32 +159,31 @@ __global__ __launch_bounds__(256) void k_attn_bwd_pre(AttnBwdArgs a) {
 // dk, dv: one workgroup per (segment, head, 128-key block)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a) {
-    // distinct LDS objects, so loads into one buffer never look like they alias reads of another
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kBwdKBlock * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kBwdKBlock * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sQ0[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sQ1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ2[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sE0[kTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t sE1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint32_t sP0[(kBwdKBlock / 32) * 2 * 64 * 8];
+    __shared__ __attribute__((aligned(16))) uint32_t sP1[(kBwdKBlock / 32) * 2 * 64 * 8];
     __shared__ __attribute__((aligned(16))) float sL0[kBN];
     __shared__ __attribute__((aligned(16))) float sL1[kBN];
     __shared__ __attribute__((aligned(16))) float sD0[kBN];
     __shared__ __attribute__((aligned(16))) float sD1[kBN];
-    __shared__ __attribute__((aligned(16))) uint32_t sP[(kBwdKBlock / 32) * 2 * 64 * 8];
 
     const int lo = find_entry(a, blockIdx.x);
     const int seg_len = a.seg_len[lo];
     const int kblocks = (seg_len + kBwdKBlock - 1) / kBwdKBlock;
     const int local = blockIdx.x - a.wg_prefix[lo];
     const int head = local / kblocks;
-    const int key0 = (local - head * kblocks) * kBwdKBlock;          // segment-relative first key
+    const int key0 = (local - head * kblocks) * kBwdKBlock;
     const uint64_t row_stride = (uint64_t)a.n_heads * kD;
     const uint64_t seg_row0 = (uint64_t)a.seg_begin[lo];
     const uint64_t base = seg_row0 * row_stride + (uint64_t)head * kD;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const int kb = wave & 3;             // key block of this wave: keys key0 + 32*kb ..
-    const bool dv_wave = (wave >> 2) != 0;   // waves 0-3 accumulate dK, waves 4-7 dV
+    const int kb = wave & 3;
+    const bool dv_wave = (wave >> 2) != 0;
     const int row_bytes = (int)(row_stride * 2);
 
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base;
@@ -191,11 +191,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
     const uint16_t *ep = static_cast<const uint16_t *>(a.e) + base;
 
-    // LDS rows loaded by this lane: 4*(kWaves*i + wave) + lane/16, chunk (lane%16) ^ f(row)
     const int ld_row0 = 4 * wave + (lane >> 4);
     const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
 
-    // ---- the block's keys and values, once -------------------------------------------
+    // ---- the key block is staged through buffers that are not live yet: K rows 0-63 in sQ1, 64-127 in
+    // sQ2, V rows 0-63 in sE1, 64-127 in sP0 (viewed as bf16 rows) ----------------------------------
+    uint16_t *const sP0h = reinterpret_cast<uint16_t *>(sP0);
     {
         const uint64_t blk0 = (uint64_t)key0 * row_stride;
         const __amdgpu_buffer_rsrc_t rk =
@@ -208,9 +209,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             int key = ld_row0 + 4 * kWaves * i;
             key = key < last ? key : last;
             const int off = key * row_bytes + ld_chunk * 16;
-            const int lds_row = 4 * (kWaves * i + wave);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK + lds_row * kD), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV + lds_row * kD), 16, off, 0, 0, 0);
+            const int lds_row = 4 * (kWaves * i + wave);             // 0..127; i < 2 -> rows < 64
+            uint16_t *kdst = (i < 2 ? sQ1 : sQ2) + (lds_row & 63) * kD;
+            uint16_t *vdst = (i < 2 ? sE1 : sP0h) + (lds_row & 63) * kD;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)kdst, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)vdst, 16, off, 0, 0, 0);
         }
     }
     const int n_qt = (seg_len + kBN - 1) / kBN;
@@ -237,142 +240,148 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + lds_row * kD), 16, off, 0, 0, 0);
         }
     };
-    // lse (base 2, +inf past the segment end) and -D of a query tile: wave 0 and wave 1, one value per lane
-    // (-D seeds the dP accumulator, so the MFMA chain yields dP - D)
     auto row_value = [&](int qt) -> float {
         const int qrow = qt * kBN + lane;
-        if (wave == 0) {
+        if (wave == 0)
             return qrow < seg_len ? a.lse[(seg_row0 + qrow) * a.n_heads + head] * kLog2e : __builtin_inff();
-        }
         return qrow < seg_len ? -a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
     };
 
-    // per-lane LDS offsets: row l32 of a 32-row block, chunk 2ks+half (f(row) repeats every 16 rows,
-    // so the same offsets serve the query half qsel*32 of a tile and the key block kb*32)
     const CompactOffsets coff = compact_offsets(lane);
-    const int k_base = __builtin_amdgcn_readfirstlane(kb * 32 * kD);     // this wave's key block
-
-    f32x16 acc[kD / 32];         // dK^T or dV^T of the wave's 32 keys: lane = key, registers = channels
+    f32x16 acc[kD / 32];
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
+    bf16x8 fixed_op[kD / 16];            // K fragments of the wave's keys (dV wave) or their V fragments (dK wave)
+    f32x16 dp[2];                        // dK wave: dP - D of the previous tile, carried over the barrier
+    const int p_off = (kb * 4 * 64 + lane) * 4;
 
-    // P of the tile in bf16, handed from each dV wave to the dK wave of the same key block
-    // (kb = wave % 4 for both), in the register layout of both waves' MFMA results:
-    // [key block][query half][word quad][lane][4 words], 16 consecutive bytes per lane
-    uint32_t *const p_mine = sP + (kb * 4 * 64 + lane) * 4;
-
-    auto compute_tile = [&](const uint16_t *tq, const uint16_t *te, const float *tl, const float *td) {
-        // The LDS objects span more than the 64 KB a read's immediate offset reaches, so every
-        // (object, offset) pair needs its own address register: the offsets are expanded here,
-        // per tile, rather than kept live across the loop.
+    // dV wave, tile qt: S, P (published to pw_dst), dV += e^T P
+    auto dv_step = [&](const uint16_t *tq, const uint16_t *te, const float *tl, uint32_t *pw_dst) {
         int ro[kD / 16], to[kD / 32][2];
         expand_offsets(coff, ro, to);
-        // phase 1: the dV wave forms S = Q K^T and P (lane = key; register r holds query row
-        // qh*32 + 8*(r/4) + 4*half + r%4) and publishes P; the dK wave forms dP = e V^T
-        uint32_t pw[2][8];
-        f32x16 dp[2];
-        // each K (V) fragment of the wave's keys is read once and used for both 32-query halves
-        if (dv_wave) {
-            f32x16 sc[2] = {};
+        f32x16 sc[2] = {};
 #pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks) {
-                const bf16x8 kf = lds_b128(sK + k_base + ro[ks]);
-#pragma unroll
-                for (int qh = 0; qh < 2; ++qh)
-                    sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + qh * 32 * kD + ro[ks]), kf,
-                                                                     sc[qh], 0, 0, 0);
-            }
-#pragma unroll
-            for (int qh = 0; qh < 2; ++qh) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
-                    float pr[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qh][4 * i + e], a.scale_log2, -lv[e]));
-                    pw[qh][2 * i] = pack_bf16x2(pr[0], pr[1]);
-                    pw[qh][2 * i + 1] = pack_bf16x2(pr[2], pr[3]);
-                }
-                *reinterpret_cast<u32x4 *>(p_mine + qh * 512) = (u32x4){pw[qh][0], pw[qh][1], pw[qh][2], pw[qh][3]};
-                *reinterpret_cast<u32x4 *>(p_mine + qh * 512 + 256) =
-                    (u32x4){pw[qh][4], pw[qh][5], pw[qh][6], pw[qh][7]};
-            }
-        } else {
-            // dP - D: the accumulator starts from -D of each register's query row
+        for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 nd = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dp[qh][4 * i + e] = nd[e];
-                }
-#pragma unroll
-            for (int ks = 0; ks < kD / 16; ++ks) {
-                const bf16x8 vf = lds_b128(sV + k_base + ro[ks]);
-#pragma unroll
-                for (int qh = 0; qh < 2; ++qh)
-                    dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + qh * 32 * kD + ro[ks]), vf,
-                                                                     dp[qh], 0, 0, 0);
-            }
+                sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + qh * 32 * kD + ro[ks]), fixed_op[ks],
+                                                                 sc[qh], 0, 0, 0);
         }
-        __syncthreads();                                 // P of the whole tile is in LDS
-        // phase 2: dV^T += e^T P (dV wave); dS = P (dP - D), dK^T += Q^T dS (dK wave; dp holds dP - D)
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
-            const int q_base = qh * 32 * kD;
-            uint32_t w[8];
-            if (dv_wave) {
+            uint32_t pw[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w[i] = pw[qh][i];
-            } else {
-                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(p_mine + qh * 512);
-                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(p_mine + qh * 512 + 256);
-                const uint32_t pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
+                float pr[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * dp[qh][4 * i], bf16_hi(pr[2 * i]) * dp[qh][4 * i + 1]);
-                    w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * dp[qh][4 * i + 2],
-                                               bf16_hi(pr[2 * i + 1]) * dp[qh][4 * i + 3]);
-                }
+                for (int e = 0; e < 4; ++e)
+                    pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qh][4 * i + e], a.scale_log2, -lv[e]));
+                pw[2 * i] = pack_bf16x2(pr[0], pr[1]);
+                pw[2 * i + 1] = pack_bf16x2(pr[2], pr[3]);
             }
-            const uint16_t *tt = dv_wave ? te : tq;      // e^T for dV, Q^T for dK
+            *reinterpret_cast<u32x4 *>(pw_dst + p_off + qh * 512) = (u32x4){pw[0], pw[1], pw[2], pw[3]};
+            *reinterpret_cast<u32x4 *>(pw_dst + p_off + qh * 512 + 256) = (u32x4){pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {                // 16-query step j uses registers 8j..8j+7
-                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
 #pragma unroll
                 for (int db = 0; db < kD / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tt + q_base + 16 * j * kD, to, db), b,
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(te + qh * 32 * kD + 16 * j * kD, to, db), b,
                                                                       acc[db], 0, 0, 0);
             }
         }
     };
+    // dK wave: dS of the previous tile from its P (published last tile) and the carried dP - D, dK += Q^T dS
+    auto dk_finish = [&](const uint16_t *tq_prev, const uint32_t *p_src) {
+        int ro[kD / 16], to[kD / 32][2];
+        expand_offsets(coff, ro, to);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+            const u32x4 p0 = *reinterpret_cast<const u32x4 *>(p_src + p_off + qh * 512);
+            const u32x4 p1 = *reinterpret_cast<const u32x4 *>(p_src + p_off + qh * 512 + 256);
+            const uint32_t pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * dp[qh][4 * i], bf16_hi(pr[2 * i]) * dp[qh][4 * i + 1]);
+                w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * dp[qh][4 * i + 2], bf16_hi(pr[2 * i + 1]) * dp[qh][4 * i + 3]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tq_prev + qh * 32 * kD + 16 * j * kD, to, db), b,
+                                                                      acc[db], 0, 0, 0);
+            }
+        }
+    };
+    // dK wave, tile qt: dP - D, seeded with -D of each register's query row
+    auto dk_start = [&](const uint16_t *te, const float *td) {
+        int ro[kD / 16], to[kD / 32][2];
+        expand_offsets(coff, ro, to);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 nd = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp[qh][4 * i + e] = nd[e];
+            }
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + qh * 32 * kD + ro[ks]), fixed_op[ks],
+                                                                 dp[qh], 0, 0, 0);
+        }
+    };
 
-    // ---- prologue: tile 0 -----------------------------------------------------------
+    // ---- prologue ----------------------------------------------------------------------------
     issue_tile(0, sQ0, sE0);
-    if (wave < 2) {
-        const float rv = row_value(0);
-        (wave == 0 ? sL0 : sD0)[lane] = rv;
+    if (wave < 2) (wave == 0 ? sL0 : sD0)[lane] = row_value(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();                                  // key block and tile 0 landed
+    {
+        int ro0[kD / 16], to0[kD / 32][2];
+        expand_offsets(coff, ro0, to0);
+        const uint16_t *blk = dv_wave ? (kb < 2 ? sQ1 : sQ2) : (kb < 2 ? sE1 : sP0h);
+        blk += (kb & 1) * 32 * kD;
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) fixed_op[ks] = lds_b128(blk + ro0[ks]);
     }
-    // ---- main loop over query tiles; the double buffers alternate by tile parity (one
-    // instance of the tile body: unrolled by two, the register allocator moved the
-    // accumulators to a second register range every other tile)
-    for (int qt = 0; qt < n_qt; ++qt) {
+    __syncthreads();                                  // the staging buffers are free again
+
+    // ---- one barrier per tile; the dK wave finishes tile qt-1 in tile qt ---------------------------
+    for (int qt = 0; qt <= n_qt; ++qt) {
+        if (qt > 0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+        }
+        const int m3 = qt % 3;
         const bool odd = (qt & 1) != 0;
-        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): this lane's loads of tile qt landed
-        __syncthreads();
+        uint16_t *q_cur = m3 == 0 ? sQ0 : (m3 == 1 ? sQ1 : sQ2);
+        uint16_t *q_next = m3 == 0 ? sQ1 : (m3 == 1 ? sQ2 : sQ0);
+        uint16_t *q_prev = m3 == 0 ? sQ2 : (m3 == 1 ? sQ0 : sQ1);
+        uint16_t *e_cur = odd ? sE1 : sE0, *e_next = odd ? sE0 : sE1;
+        uint32_t *p_cur = odd ? sP1 : sP0, *p_prev = odd ? sP0 : sP1;
+        const float *l_cur = odd ? sL1 : sL0, *d_cur = odd ? sD1 : sD0;
         float nv = 0.f;
         if (qt + 1 < n_qt) {
-            issue_tile(qt + 1, odd ? sQ0 : sQ1, odd ? sE0 : sE1);
+            issue_tile(qt + 1, q_next, e_next);
             if (wave < 2) nv = row_value(qt + 1);
         }
-        compute_tile(odd ? sQ1 : sQ0, odd ? sE1 : sE0, odd ? sL1 : sL0, odd ? sD1 : sD0);
+        if (dv_wave) {
+            if (qt < n_qt) dv_step(q_cur, e_cur, l_cur, p_cur);
+        } else {
+            if (qt > 0) dk_finish(q_prev, p_prev);
+            if (qt < n_qt) dk_start(e_cur, d_cur);
+        }
         if (qt + 1 < n_qt && wave < 2) (wave == 0 ? (odd ? sL0 : sL1) : (odd ? sD0 : sD1))[lane] = nv;
     }
 
-    // ---- store this wave's 32 keys: lane = key, register r = channel db*32 + 8*(r/4) + 4*half + r%4
-    const int key = key0 + kb * 32 + l32;             // segment-relative key of this lane
+    const int key = key0 + kb * 32 + l32;
     if (key >= seg_len) return;
     uint16_t *outp = static_cast<uint16_t *>(dv_wave ? a.dv : a.dk) + base + (uint64_t)key * row_stride;
     const float mul = dv_wave ? 1.0f : a.scale;
@@ -380,7 +389,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-            const int d0 = db * 32 + 8 * (r / 4) + 4 * half;      // 4 consecutive channels
+            const int d0 = db * 32 + 8 * (r / 4) + 4 * half;
             const u32x2 w = {pack_bf16x2(acc[db][r] * mul, acc[db][r + 1] * mul),
                              pack_bf16x2(acc[db][r + 2] * mul, acc[db][r + 3] * mul)};
             *reinterpret_cast<u32x2 *>(outp + d0) = w;
