@@ -39,8 +39,13 @@
 // are masked to -inf (dq kernel), queries there get lse = +inf so their p is 0
 // (dk/dv kernel), and no output row past the end is written.
 //
-// MFMA layouts (v_mfma_f32_32x32x16_bf16) follow packed_attn.hip; the LDS
-// swizzle and the transposing read are those of h3_device.h.
+// MFMA layouts (v_mfma_f32_32x32x16_bf16) and the transposing read follow
+// packed_attn.hip.  The streamed 64-row tiles (K and V in the dq kernel, Q and
+// e in the dk/dv kernel) use a padded LDS layout instead of the forward's XOR
+// swizzle: it is as free of bank conflicts, and because each chunk of a row
+// sits at a constant distance from the row start, one lane base and immediate
+// offsets address every read of a tile whichever buffer holds it, so the
+// single tile body computes no addresses per tile.
 #include "h3_device.h"
 
 namespace h3 {
@@ -48,9 +53,7 @@ namespace h3 {
 namespace {
 
 constexpr int kBN = 64;                  // keys per tile (dq) / queries per tile (dk/dv)
-constexpr int kTileElems = kBN * kD;
 constexpr int kWaves = kBwdThreads / 64; // 8
-constexpr int kLoadsPerTile = kBN / (4 * kWaves);          // 16-byte loads per lane per 64-row tile
 constexpr int kLoadsPerKBlock = kBwdKBlock / (4 * kWaves); // per 128-row key block
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdQBlock == 32 * kWaves, "one 32-query block per wave");
@@ -62,55 +65,50 @@ __device__ __forceinline__ bf16x8 lds_b128(const uint16_t *p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
-// offsets of the transposing reads that give the A operand X^T (32 channels x
-// 16 rows) of a 16-row step from a row-major tile X: k slot (half, jj) of the
-// step is tile row 8*(jj/4) + 4*half + jj%4, as the C layout orders rows
-__device__ __forceinline__ void tr_offsets(int lane, int (&off)[kD / 32][2]) {
-    const int half = lane >> 5, grp = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int r = 8 * s2 + 4 * half + (i >> 2);
-            const int col = db * 32 + 16 * (grp & 1) + 4 * (i & 3);
-            off[db][s2] = swz(r, col >> 3) + (col & 7);
-        }
-}
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *tile_rows, const int (&off)[kD / 32][2], int db) {
-    const bf16x4 a = lds_read_tr(tile_rows + off[db][0]);
-    const bf16x4 b = lds_read_tr(tile_rows + off[db][1]);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+// Padded LDS layout of a 64-row tile, in 16-byte slots: row r = 4k + a starts
+// at slot 77k + 20a and its 16 chunks follow in order.  The slot of (r, c) is
+// then f(r) + c mod 16 with f(r) = 4a + 13k mod 16, so 16 rows of an aligned
+// group read at one chunk, and the 4 rows x 4 chunks of a transposing read,
+// each hit 16 distinct bank groups -- the XOR swizzle's property -- while
+// every chunk of a lane's row is its row start plus a constant: all reads of
+// a tile are one lane base and immediate offsets, whichever buffer the tile
+// is in.  The layout spends 13 padding slots per 4 rows (1232 slots for 64
+// rows), filled by 20 direct loads of 64 slots.
+constexpr int kPadGroupSlots = 77;                      // 4 rows of 16 slots + 13 padding slots
+constexpr int kPadRowSlots = 20;
+constexpr int kPadTileLoads = 20;                       // 1 KB direct loads per tile (1280 slots)
+constexpr int kPadTileElems = kPadTileLoads * 64 * 8;   // bf16 elements per tile buffer (20 KB)
+constexpr int kPad4Rows = kPadGroupSlots * 8;           // elements between rows r and r + 4
+static_assert(kBN / 4 * kPadGroupSlots <= kPadTileLoads * 64, "the loads cover the padded tile");
+
+// element offset of (row r, chunk 0) in a padded tile
+__device__ __forceinline__ int pad_row(int r) { return 8 * (kPadGroupSlots * (r >> 2) + kPadRowSlots * (r & 3)); }
+
+// the tile row and chunk that slot `lane` of direct load i holds; padding slots
+// (and slots past the tile) re-read chunk 15 of their row, or row 63
+__device__ __forceinline__ void pad_slot(int i, int lane, int &row, int &chunk) {
+    const int p = 64 * i + lane;
+    const int k = p / kPadGroupSlots;
+    const int q = p - kPadGroupSlots * k;
+    const int a = q / kPadRowSlots < 3 ? q / kPadRowSlots : 3;
+    const int r = 4 * k + a, c = q - kPadRowSlots * a;
+    row = r < kBN - 1 ? r : kBN - 1;
+    chunk = c < 15 ? c : 15;
 }
 
-// The same offsets in closed form, from three per-lane values, for kernels short of registers:
-//   swz(l32, 2ks + half)  = rb + ((ks ^ rx) << 4)
-//   tr offset (db, s2)    = tb[s2] + ((db ^ tx) << 5)
-struct CompactOffsets {
-    int rb, rx, tb0, tb1, tx;
-};
-__device__ __forceinline__ CompactOffsets compact_offsets(int lane) {
-    const int l32 = lane & 31, half = lane >> 5, grp = lane >> 4, i = lane & 15;
-    const int f = swz_f(l32);
-    CompactOffsets c;
-    c.rb = l32 * kD + 8 * (half ^ (f & 1));
-    c.rx = f >> 1;
-    const int c0 = 2 * (grp & 1) + ((i & 3) >> 1);
-    c.tb0 = (4 * half + (i >> 2)) * kD + 8 * (c0 ^ half) + 4 * (i & 1);
-    c.tb1 = (8 + 4 * half + (i >> 2)) * kD + 8 * (c0 ^ (2 + half)) + 4 * (i & 1);
-    c.tx = i >> 2;
-    return c;
+// lane bases in a padded tile: the A operand read (row l32, chunk 2ks + half is
+// pad_a + 16 ks) and the transposing read (tile row 8 s2 + 4 half + i/4,
+// channels 32 db + 16 (grp&1) + 4 (i&3) .. +3 is pad_t + 1232 s2 + 32 db)
+__device__ __forceinline__ int pad_a_base(int lane) { return pad_row(lane & 31) + 8 * (lane >> 5); }
+__device__ __forceinline__ int pad_t_base(int lane) {
+    const int half = lane >> 5, grp = lane >> 4, i = lane & 15;
+    return pad_row(4 * half + (i >> 2)) + 16 * (grp & 1) + 4 * (i & 3);
 }
-// Expand inside a tile's work; the empty asm keeps the expansion from being hoisted out of the
-// loop (where every (LDS object, offset) address would stay live across it).
-__device__ __forceinline__ void expand_offsets(CompactOffsets c, int (&ro)[kD / 16], int (&to)[kD / 32][2]) {
-    asm volatile("" : "+v"(c.rb), "+v"(c.rx), "+v"(c.tb0), "+v"(c.tb1), "+v"(c.tx));
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) ro[ks] = c.rb + ((ks ^ c.rx) << 4);
-#pragma unroll
-    for (int db = 0; db < kD / 32; ++db) {
-        to[db][0] = c.tb0 + ((db ^ c.tx) << 5);
-        to[db][1] = c.tb1 + ((db ^ c.tx) << 5);
-    }
+// X^T fragment (32 channels x 16 tile rows) from a padded tile; rows points at row 16j's group
+__device__ __forceinline__ bf16x8 pad_tr_frag(const uint16_t *rows, int db) {
+    const bf16x4 a = lds_read_tr(rows + 32 * db);
+    const bf16x4 b = lds_read_tr(rows + 2 * kPad4Rows + 32 * db);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // which (entry, local index) a workgroup id belongs to in a longest-first work list
@@ -159,11 +157,11 @@ __global__ __launch_bounds__(256) void k_attn_bwd_pre(AttnBwdArgs a) {
 // dk, dv: one workgroup per (segment, head, 128-key block)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ2[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sE0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sE1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ2[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sE0[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sE1[kPadTileElems];
     __shared__ __attribute__((aligned(16))) uint32_t sP0[(kBwdKBlock / 32) * 2 * 64 * 8];
     __shared__ __attribute__((aligned(16))) uint32_t sP1[(kBwdKBlock / 32) * 2 * 64 * 8];
     __shared__ __attribute__((aligned(16))) float sL0[kBN];
@@ -195,7 +193,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
 
     // ---- the key block is staged through buffers that are not live yet: K rows 0-63 in sQ1, 64-127 in
-    // sQ2, V rows 0-63 in sE1, 64-127 in sP0 (viewed as bf16 rows) ----------------------------------
+    // sQ2, V rows 0-63 in sE1, 64-127 in sP0 (viewed as bf16 rows).  It is read once, so it keeps the
+    // compact XOR-swizzled layout of h3_device.h (16 KB per 64 rows) --------------------------------
     uint16_t *const sP0h = reinterpret_cast<uint16_t *>(sP0);
     {
         const uint64_t blk0 = (uint64_t)key0 * row_stride;
@@ -216,10 +215,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)vdst, 16, off, 0, 0, 0);
         }
     }
+    // Q and e tiles use the padded layout: direct loads i = wave + 8m (three for waves 0-3, two for 4-7)
+    constexpr int kLdPerWave = (kPadTileLoads + kWaves - 1) / kWaves;
     const int n_qt = (seg_len + kBN - 1) / kBN;
-    int ld_off[kLoadsPerTile];
+    int ld_off[kLdPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerTile; ++i) ld_off[i] = (ld_row0 + 4 * kWaves * i) * row_bytes + ld_chunk * 16;
+    for (int m = 0; m < kLdPerWave; ++m) {
+        int row, chunk;
+        pad_slot(wave + kWaves * m, lane, row, chunk);
+        ld_off[m] = row * row_bytes + chunk * 16;
+    }
     auto issue_tile = [&](int qt, uint16_t *dq_, uint16_t *de_) {
         const uint64_t tile0 = (uint64_t)qt * kBN * row_stride;
         const __amdgpu_buffer_rsrc_t rq =
@@ -228,16 +233,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             __builtin_amdgcn_make_buffer_rsrc((void *)(ep + tile0), 0, kBN * row_bytes, kBufferWord3);
         const int last = seg_len - 1 - qt * kBN;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerTile; ++i) {
-            int off = ld_off[i];
+        for (int m = 0; m < kLdPerWave; ++m) {
+            const int i = wave + kWaves * m;                  // wave-uniform
+            if (i >= kPadTileLoads) break;
+            int off = ld_off[m];
             if ((qt + 1) * kBN > seg_len) {
-                int row = ld_row0 + 4 * kWaves * i;
+                int row, chunk;
+                pad_slot(i, lane, row, chunk);
                 row = row < last ? row : last;
-                off = row * row_bytes + ld_chunk * 16;
+                off = row * row_bytes + chunk * 16;
             }
-            const int lds_row = 4 * (kWaves * i + wave);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dq_ + lds_row * kD), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dq_ + i * 512), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + i * 512), 16, off, 0, 0, 0);
         }
     };
     auto row_value = [&](int qt) -> float {
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
         return qrow < seg_len ? -a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
     };
 
-    const CompactOffsets coff = compact_offsets(lane);
+    const int pa = pad_a_base(lane), pt = pad_t_base(lane);
     f32x16 acc[kD / 32];
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
@@ -257,15 +264,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
 
     // dV wave, tile qt: S, P (published to pw_dst), dV += e^T P
     auto dv_step = [&](const uint16_t *tq, const uint16_t *te, const float *tl, uint32_t *pw_dst) {
-        int ro[kD / 16], to[kD / 32][2];
-        expand_offsets(coff, ro, to);
         f32x16 sc[2] = {};
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh)
-                sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + qh * 32 * kD + ro[ks]), fixed_op[ks],
-                                                                 sc[qh], 0, 0, 0);
+                sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + pa + 8 * kPad4Rows * qh + 16 * ks),
+                                                                 fixed_op[ks], sc[qh], 0, 0, 0);
         }
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
@@ -287,15 +292,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
                 const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
 #pragma unroll
                 for (int db = 0; db < kD / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(te + qh * 32 * kD + 16 * j * kD, to, db), b,
-                                                                      acc[db], 0, 0, 0);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        pad_tr_frag(te + pt + kPad4Rows * (8 * qh + 4 * j), db), b, acc[db], 0, 0, 0);
             }
         }
     };
     // dK wave: dS of the previous tile from its P (published last tile) and the carried dP - D, dK += Q^T dS
     auto dk_finish = [&](const uint16_t *tq_prev, const uint32_t *p_src) {
-        int ro[kD / 16], to[kD / 32][2];
-        expand_offsets(coff, ro, to);
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
             const u32x4 p0 = *reinterpret_cast<const u32x4 *>(p_src + p_off + qh * 512);
@@ -312,15 +315,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
                 const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
 #pragma unroll
                 for (int db = 0; db < kD / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tq_prev + qh * 32 * kD + 16 * j * kD, to, db), b,
-                                                                      acc[db], 0, 0, 0);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        pad_tr_frag(tq_prev + pt + kPad4Rows * (8 * qh + 4 * j), db), b, acc[db], 0, 0, 0);
             }
         }
     };
     // dK wave, tile qt: dP - D, seeded with -D of each register's query row
     auto dk_start = [&](const uint16_t *te, const float *td) {
-        int ro[kD / 16], to[kD / 32][2];
-        expand_offsets(coff, ro, to);
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
@@ -333,8 +334,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
         for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh)
-                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + qh * 32 * kD + ro[ks]), fixed_op[ks],
-                                                                 dp[qh], 0, 0, 0);
+                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + pa + 8 * kPad4Rows * qh + 16 * ks),
+                                                                 fixed_op[ks], dp[qh], 0, 0, 0);
         }
     };
 
@@ -344,12 +345,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();                                  // key block and tile 0 landed
     {
-        int ro0[kD / 16], to0[kD / 32][2];
-        expand_offsets(coff, ro0, to0);
         const uint16_t *blk = dv_wave ? (kb < 2 ? sQ1 : sQ2) : (kb < 2 ? sE1 : sP0h);
         blk += (kb & 1) * 32 * kD;
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) fixed_op[ks] = lds_b128(blk + ro0[ks]);
+        for (int ks = 0; ks < kD / 16; ++ks) fixed_op[ks] = lds_b128(blk + swz(l32, 2 * ks + half));
     }
     __syncthreads();                                  // the staging buffers are free again
 
@@ -400,10 +399,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
 // dq: one workgroup per (segment, head, 256-query tile), lane = query
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sK1[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sV0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sV1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kPadTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kPadTileElems];
 
     const int lo = find_entry(a, blockIdx.x);
     const int seg_len = a.seg_len[lo];
@@ -444,14 +443,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     const float lse2 = a.lse[lrow] * kLog2e;
     const float delta = a.delta[lrow];
 
-    const CompactOffsets coff = compact_offsets(lane);
+    const int pa = pad_a_base(lane), pt = pad_t_base(lane);
 
-    const int ld_row0 = 4 * wave + (lane >> 4);
-    const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
+    // direct loads i = wave + 8m of each padded tile (three for waves 0-3, two for 4-7)
+    constexpr int kLdPerWave = (kPadTileLoads + kWaves - 1) / kWaves;
     const int n_kt = (seg_len + kBN - 1) / kBN;
-    int ld_off[kLoadsPerTile];
+    int ld_off[kLdPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerTile; ++i) ld_off[i] = (ld_row0 + 4 * kWaves * i) * row_bytes + ld_chunk * 16;
+    for (int m = 0; m < kLdPerWave; ++m) {
+        int row, chunk;
+        pad_slot(wave + kWaves * m, lane, row, chunk);
+        ld_off[m] = row * row_bytes + chunk * 16;
+    }
     auto issue_tile = [&](int kt, uint16_t *dk_, uint16_t *dv_) {
         const uint64_t tile0 = (uint64_t)kt * kBN * row_stride;
         const __amdgpu_buffer_rsrc_t rk =
@@ -460,16 +463,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
             __builtin_amdgcn_make_buffer_rsrc((void *)(vp + tile0), 0, kBN * row_bytes, kBufferWord3);
         const int last = seg_len - 1 - kt * kBN;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerTile; ++i) {
-            int off = ld_off[i];
+        for (int m = 0; m < kLdPerWave; ++m) {
+            const int i = wave + kWaves * m;                  // wave-uniform
+            if (i >= kPadTileLoads) break;
+            int off = ld_off[m];
             if ((kt + 1) * kBN > seg_len) {
-                int key = ld_row0 + 4 * kWaves * i;
-                key = key < last ? key : last;
-                off = key * row_bytes + ld_chunk * 16;
+                int row, chunk;
+                pad_slot(i, lane, row, chunk);
+                row = row < last ? row : last;
+                off = row * row_bytes + chunk * 16;
             }
-            const int lds_row = 4 * (kWaves * i + wave);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk_ + lds_row * kD), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv_ + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dk_ + i * 512), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dv_ + i * 512), 16, off, 0, 0, 0);
         }
     };
 
@@ -478,8 +483,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
 
     auto compute_tile = [&](int kt, const uint16_t *tk, const uint16_t *tv) {
-        int k_off[kD / 16], t_off[kD / 32][2];
-        expand_offsets(coff, k_off, t_off);
         // one 32-key block at a time: S^T = K Q^T and dP^T = V e^T (lane = query), then
         // dS^T = P^T (dP^T - D) packed as the B operand of two 16-key steps, then dQ^T += K^T dS^T
 #pragma unroll
@@ -487,9 +490,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
             f32x16 s = {}, dp = {};
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tk + kb * 32 * kD + k_off[ks]), qreg[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tv + kb * 32 * kD + k_off[ks]), ereg[ks], dp, 0, 0,
-                                                             0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tk + pa + 8 * kPad4Rows * kb + 16 * ks), qreg[ks], s, 0,
+                                                            0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tv + pa + 8 * kPad4Rows * kb + 16 * ks), ereg[ks], dp,
+                                                             0, 0, 0);
             }
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_frag(tk + (kb * 32 + 16 * j) * kD, t_off, db), dsb[j], acc[db], 0, 0, 0);
+                        pad_tr_frag(tk + pt + kPad4Rows * (8 * kb + 4 * j), db), dsb[j], acc[db], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
             for (int i = 0; i < 6; ++i) {
