@@ -441,7 +441,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     }
     const uint64_t lrow = (seg_row0 + (uint64_t)(q_valid ? q_local : 0)) * a.n_heads + head;
     const float lse2 = a.lse[lrow] * kLog2e;
-    const float delta = a.delta[lrow];
+    // -D of this lane's query in every register: the start value of each dP^T accumulation, so that
+    // the accumulator ends as dP^T - D (every register of the C layout belongs to the lane's query)
+    f32x16 neg_delta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) neg_delta[r] = -a.delta[lrow];
 
     const int pa = pad_a_base(lane), pt = pad_t_base(lane);
 
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
         // dS^T = P^T (dP^T - D) packed as the B operand of two 16-key steps, then dQ^T += K^T dS^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s = {}, dp = {};
+            f32x16 s = {}, dp = neg_delta;
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tk + pa + 8 * kPad4Rows * kb + 16 * ks), qreg[ks], s, 0,
@@ -502,7 +506,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-            if ((kt + 1) * kBN > seg_len) {
+            if (__builtin_expect((kt + 1) * kBN > seg_len, 0)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kt * kBN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
                     const int r = 8 * j + 2 * e;
                     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -lse2));
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], a.scale_log2, -lse2));
-                    w4[e] = pack_bf16x2(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+                    w4[e] = pack_bf16x2(p0 * dp[r], p1 * dp[r + 1]);
                 }
                 dsb[j] = __builtin_bit_cast(bf16x8, (u32x4){w4[0], w4[1], w4[2], w4[3]});
             }
