@@ -12,9 +12,9 @@ Prints ONE JSON line.  ``value`` is the packed-attention throughput in TFLOP/s
 (algorithmic FLOPs of the step's attention / time of its attention launch);
 relayout and AdaLN rates are reported under ``components``; the backward
 pass (relayout adjoints and attention backward), timed after the step, under
-``backward``; the gated AdaLN chain, the ragged reduce-scatter and the ragged
-row gather, also timed after the step, under ``token_sharded_ops``.
-``roofline``
+``backward``; AdaLN's residual gating, the gated AdaLN chain, the ragged
+reduce-scatter and the ragged row gather, also timed after the step, under
+``token_sharded_ops``.  ``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on this host's cores.
@@ -203,8 +203,10 @@ def measure_backward(w, reps: int = 5) -> dict:
 
 def measure_next(step, reps: int = 5) -> dict:
     """The token-sharded blocks' ops at the same workload, timed with HIP
-    events after the timed steps (not part of ``value``): the gated AdaLN chain
-    over every rank interval (x, branch -> residual, modulated y), the ragged
+    events after the timed steps (not part of ``value``): AdaLN's residual
+    gating (GATE mode: y = x + gate * branch) over every rank interval, the
+    gated AdaLN chain over every rank interval (x, branch -> residual,
+    modulated y), the ragged
     reduce-scatter of P partial outputs [N, C] with bias for every rank, and
     the ragged row gather of the P token shards back to [N, C]."""
     import torch
@@ -235,6 +237,14 @@ def measure_next(step, reps: int = 5) -> dict:
 
     branch = normal_bf16((n, c), seed=4300, device="cuda")
     resid, y = torch.empty_like(branch), torch.empty_like(branch)
+
+    def gate():
+        return [h3.adaln_segment(h3.H3_ADALN_GATE_RESIDUAL, step.x[a:a + cnt], branch[a:a + cnt], None, None,
+                                 step.gate, y[a:a + cnt], a, a + cnt, step.cu, 0.0, stream=st)
+                for a, cnt in step.tokens]
+
+    ms, infos = timed(gate)
+    out["adaln_gate"] = entry(ms, 3 * n * row, len(infos))
 
     def chain():
         return [h3.adaln_gate_modulate(step.x[a:a + cnt], branch[a:a + cnt], step.gate, step.shift, step.ada_scale,
