@@ -123,6 +123,37 @@ def cpu_baseline(step, workload, budget_s: float):
     adaln_s = time.perf_counter() - t0
     rate = flops / spent
 
+    # the next rows' oracle, timed beside their kernels (their parity is in the GPU tests)
+    next_rows = {}
+    dout = v                      # the value plane doubles as a synthetic N(0,1) output gradient
+    bw_rows, bw_flops, bw_spent = 0, 0.0, 0.0
+    while bw_spent < budget_s / 4:
+        rows = np.sort(rng.integers(0, step.n_tokens, size=8))
+        t0 = time.perf_counter()
+        oracle.attention_backward(q, k, v, g, dout, cu, step.scale, q_rows=rows, k_rows=[], threads=threads)
+        bw_spent += time.perf_counter() - t0
+        seg_of = np.searchsorted(np.asarray(cu), rows, side="right") - 1
+        bw_flops += float(6 * 128 * heads * seg_len[seg_of].sum())
+        bw_rows += len(rows)
+    next_rows["attention_backward"] = {
+        "GFLOPs": bw_flops / bw_spent / 1e9, "query_rows": bw_rows, "seconds": bw_spent,
+        "flop_rule": "6 x 128 per (query, key) pair per head: S, dP and dQ of the sampled query rows"}
+    xb2 = bits(step.x[4096:8192])
+    gate = bits(step.gate)
+    t0 = time.perf_counter()
+    oracle.adaln_gate_modulate(xb, xb2, gate, prm[0], prm[1], 0, 4096, cu, step.eps, threads=threads)
+    next_rows["adaln_gate_modulate_GBps"] = 4 * xb.nbytes / (time.perf_counter() - t0) / 1e9
+    parts = [bits(step.x[i * 4096:(i + 1) * 4096]) for i in range(4)]
+    t0 = time.perf_counter()
+    oracle.reduce_scatter(parts, prm[0][0])
+    next_rows["reduce_scatter_GBps"] = 5 * xb.nbytes / (time.perf_counter() - t0) / 1e9
+    t0 = time.perf_counter()
+    oracle.gather_rows([xb[i * 1024:(i + 1) * 1024] for i in range(4)])
+    next_rows["gather_rows_GBps"] = 2 * xb.nbytes / (time.perf_counter() - t0) / 1e9
+    next_rows["sample"] = ("AdaLN chain, reduce-scatter (4 partials) and row gather (4 shards) over 4096 rows "
+                           "of 7168 channels")
+    del parts, xb2
+
     # outside the timed parts: the GPU's outputs of the last step against the oracle on the same samples
     def err(got_bits, ref):
         e = oracle.bf16_bits_to_f64(got_bits) - ref
@@ -152,6 +183,7 @@ def cpu_baseline(step, workload, budget_s: float):
         "full_attention_s_extrapolated": step.attention_flops() / rate,
         "relayout_GBps": relayout_bytes / relayout_s / 1e9,
         "adaln_GBps": 2 * xb.nbytes / adaln_s / 1e9,
+        "next_rows": next_rows,
         "parity_of_this_run": parity,
     }
 
