@@ -414,7 +414,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     const uint64_t seg_row0 = (uint64_t)a.seg_begin[lo];
     const uint64_t base = seg_row0 * row_stride + (uint64_t)head * kD;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: loads and branches are scalar
     const int q_local = qtile * kBwdQBlock + wave * 32 + l32;
     const bool q_valid = q_local < seg_len;
     const int row_bytes = (int)(row_stride * 2);

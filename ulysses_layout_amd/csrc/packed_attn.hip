@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const uint64_t base = (uint64_t)a.seg_begin[lo] * row_stride + (uint64_t)head * kD;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: load addresses are scalar
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int half = lane >> 5;
