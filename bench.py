@@ -14,7 +14,8 @@ relayout and AdaLN rates are reported under ``components``; the backward
 pass (relayout adjoints and attention backward), timed after the step, under
 ``backward``; AdaLN's residual gating, the gated AdaLN chain, the ragged
 reduce-scatter and the ragged row gather, also timed after the step, under
-``token_sharded_ops``.  ``roofline``
+``token_sharded_ops``; the same pass replayed from one captured HIP graph,
+against the pass enqueued call by call, under ``graph_step``.  ``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on this host's cores.
@@ -323,6 +324,38 @@ def run_steps(step, steps: int, warmup: int):
     return ms, wall
 
 
+def measure_graph(step, steps: int) -> dict:
+    """The whole step captured once into a HIP graph and replayed, against the
+    same step enqueued call by call: HIP events around ``steps`` passes of each.
+    The library allocates and synchronises nothing, so the capture holds every
+    launch of the pass (relayout chunks, attention, AdaLN per rank interval)."""
+    import torch
+
+    launches = sum(p.launches for plans in step.last_plans.values() for p in plans)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step.run()
+    end.record()
+    end.synchronize()
+    eager_ms = start.elapsed_time(end) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        graph.replay()
+    end.record()
+    end.synchronize()
+    graph_ms = start.elapsed_time(end) / steps
+    del graph
+    return {"launches_per_step": launches, "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+            "steps": steps}
+
+
 def make_step(w, with_backward: bool = False):
     import torch
 
@@ -366,7 +399,7 @@ def measure_workloads(names, steps: int = 3, warmup: int = 1) -> dict:
         r = step_rates(step, ms)
         r.update({"n_tokens": w.n_tokens, "segments": len(w.cu) - 1, "virtual_ranks": w.world,
                   "attention_heads": sum(step.heads[j][1] for j in step.attn_ranks), "planes": w.planes,
-                  "steps": steps})
+                  "steps": steps, "graph_step": measure_graph(step, steps)})
         out[name] = r
         del step
         torch.cuda.empty_cache()
@@ -410,6 +443,7 @@ def main():
     flops_per_launch = attn_flops / attn_launches
     launch_ms = ms["attention"] / attn_launches
     traffic = read_traffic(flops_per_launch)
+    graph_step = measure_graph(step, args.steps)
     backward = measure_backward(w)
     next_ops = measure_next(step)
     workloads = measure_workloads([n for n in args.other_workloads.split(",") if n and n != w.name])
@@ -456,6 +490,7 @@ def main():
         "relayout_frac_hbm": (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3)
         / 1e9 / PEAK_HBM_GBPS,
         "components": components,
+        "graph_step": graph_step,
         "backward": backward,
         "token_sharded_ops": next_ops,
         "workloads": workloads,
