@@ -49,6 +49,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample (attention part)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run the CPU oracle over every attention row of the rank and every AdaLN row of the first "
+                         "rank interval instead of a bounded sample (about an hour at the 128k workload)")
     ap.add_argument("--other-workloads", default="32k_p4,250k_p8_qkvg",
                     help="workloads also timed after the main one (comma list, '' for none); reported under "
                          "'workloads', never in value")
@@ -83,8 +86,10 @@ def read_traffic(flops_per_launch: float):
         return None
 
 
-def cpu_baseline(step, workload, budget_s: float):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(step, workload, budget_s: float, full: bool = False):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload
+    (with ``full``: every attention row of the rank and every AdaLN row of the
+    first rank interval, however long that takes)."""
     import numpy as np
     import torch
 
@@ -107,8 +112,14 @@ def cpu_baseline(step, workload, budget_s: float):
     seg_len = np.diff(np.asarray(cu))
     done_rows, flops, spent, sampled = 0, 0.0, 0.0, []
     heads = q.shape[1]
-    while spent < budget_s:
-        rows = np.sort(rng.integers(0, step.n_tokens, size=16))
+    full_batches = iter(np.arange(a, min(a + 256, step.n_tokens)) for a in range(0, step.n_tokens, 256))
+    while (not full and spent < budget_s) or full:
+        if full:
+            rows = next(full_batches, None)
+            if rows is None:
+                break
+        else:
+            rows = np.sort(rng.integers(0, step.n_tokens, size=16))
         t0 = time.perf_counter()
         res = oracle.attention_rows(q, k, v, g, cu, step.scale, rows=rows, threads=threads)
         spent += time.perf_counter() - t0
@@ -116,12 +127,18 @@ def cpu_baseline(step, workload, budget_s: float):
         flops += float(4 * 128 * heads * seg_len[seg_of].sum())
         done_rows += len(rows)
         sampled.append((rows, res))
-    # AdaLN modulation on the first 4096 rows of rank 0's interval
+    # AdaLN modulation on the first 4096 rows of rank 0's interval (with ``full``: all of them)
+    ada_n = step.tokens[0][1] if full else 4096
     xb = bits(step.x[:4096])
     prm = [bits(t) for t in (step.shift, step.ada_scale)]
-    t0 = time.perf_counter()
-    ada_ref = oracle.adaln_rows(0, xb, None, prm[0], prm[1], None, 0, 4096, cu, step.eps, threads=threads)
-    adaln_s = time.perf_counter() - t0
+    adaln_s, ada_parts = 0.0, []
+    for a in range(0, ada_n, 4096):
+        xa = xb if a == 0 else bits(step.x[a:min(a + 4096, ada_n)])
+        t0 = time.perf_counter()
+        ada_parts.append(oracle.adaln_rows(0, xa, None, prm[0], prm[1], None, a, a + len(xa), cu, step.eps,
+                                           threads=threads))
+        adaln_s += time.perf_counter() - t0
+    ada_ref = np.concatenate(ada_parts)
     rate = flops / spent
 
     # the next rows' oracle, timed beside their kernels (their parity is in the GPU tests)
@@ -164,11 +181,12 @@ def cpu_baseline(step, workload, budget_s: float):
     rows = np.concatenate([r for r, _ in sampled])
     attn_ref = np.concatenate([x for _, x in sampled])
     attn_err = err(bits(step.attn_out[j][torch.from_numpy(rows).cuda()]), attn_ref)
-    ada_err = err(bits(step.y[:4096]), ada_ref)
+    ada_rows = len(ada_ref)
+    ada_err = err(bits(step.y[:ada_rows]), ada_ref)
     relayout_exact = all(np.array_equal(bits(step.rank_bufs[j][p]), bufs[(j, p)]) for p in range(step.planes))
     parity = {"relayout_rank_buffers_bit_exact": relayout_exact,
               "attention_sampled_rows": int(rows.size), "attention": attn_err,
-              "adaln_rows": 4096, "adaln": ada_err,
+              "adaln_rows": ada_rows, "adaln": ada_err,
               "within_bar": bool(relayout_exact and attn_err["max_abs"] <= 2e-2 and attn_err["rel_rms"] <= 5e-3
                                  and ada_err["max_abs"] <= 2e-2 and ada_err["rel_rms"] <= 5e-3),
               # a bf16 half-ulp passes the max-abs bar only below 8
@@ -178,12 +196,14 @@ def cpu_baseline(step, workload, budget_s: float):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 attention of {done_rows} seeded random query rows x {heads} heads over their full "
-                   f"segments ({flops:.3e} FLOP in {spent:.1f} s, {rate / 1e9:.1f} GFLOP/s); relayout: oracle "
-                   f"seq2head of rank {j}'s share, all {step.planes} planes; AdaLN: 4096 modulated rows"),
+        "sample": (f"fp64 attention of {done_rows} {'' if full else 'seeded random '}query rows x {heads} heads "
+                   f"over their full segments ({flops:.3e} FLOP in {spent:.1f} s, {rate / 1e9:.1f} GFLOP/s); "
+                   f"relayout: oracle seq2head of rank {j}'s share, all {step.planes} planes; AdaLN: {ada_rows} "
+                   f"modulated rows"),
+        "full": bool(full),
         "full_attention_s_extrapolated": step.attention_flops() / rate,
         "relayout_GBps": relayout_bytes / relayout_s / 1e9,
-        "adaln_GBps": 2 * xb.nbytes / adaln_s / 1e9,
+        "adaln_GBps": 2 * ada_rows * step.channels * 2 / adaln_s / 1e9,
         "next_rows": next_rows,
         "parity_of_this_run": parity,
     }
@@ -506,7 +526,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(step, w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(step, w, args.cpu_seconds, full=args.cpu_full)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
