@@ -404,7 +404,7 @@ def step_rates(step, ms) -> dict:
             "ms": ms}
 
 
-def measure_workloads(names, steps: int = 3, warmup: int = 1) -> dict:
+def measure_workloads(names, steps: int = 5, warmup: int = 5) -> dict:
     """The same pass at the other workloads, one after another, each freed
     before the next; reported beside the main line."""
     import torch
