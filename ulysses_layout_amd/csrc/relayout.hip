@@ -38,7 +38,7 @@ __device__ __forceinline__ uint64_t packed_index(uint32_t f, FastDiv dv, uint32_
 // slower.
 template <bool kToRank>
 __device__ __forceinline__ void store_vec(u32x4 *dst, uint64_t idx, u32x4 v) {
-    if (kToRank) __builtin_nontemporal_store(v, dst + idx);
+    if constexpr (kToRank) __builtin_nontemporal_store(v, dst + idx);
     else dst[idx] = v;
 }
 
