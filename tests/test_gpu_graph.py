@@ -99,3 +99,46 @@ def test_graph_replays_match_eager(name):
     torch.cuda.synchronize()
     _assert_same(replayed, _snapshot(step), f"{name} replay on new inputs")
     del graph
+
+
+def _grads(step):
+    outs = [("grad_qkv", step.grad_qkv)]
+    for j in step.attn_ranks:
+        outs.append((f"grad_attn{j}", step.grad_attn[j]))
+        outs += [(f"grad{j}.plane{p}", t) for p, t in enumerate(step.grad_bufs[j])]
+    return outs
+
+
+@pytest.mark.parametrize("name", ["tiny512", "8k_p6", "128k_p4_qkvg"])
+def test_graph_replays_backward_match_eager(name):
+    """UlyssesStep.backward() -- head2seq adjoint, attention backward with its
+    caller-owned workspace, seq2head adjoint -- captured once and replayed."""
+    from ulysses_layout_amd.pipeline import UlyssesStep
+    w = WORKLOADS[name]
+    say("graph backward", name)
+    attn_ranks = None if w.attn_rank is None else [w.attn_rank]
+    step = UlyssesStep(w.n_tokens, w.cu, w.world, w.planes, attn_ranks=attn_ranks, relayout_rank=w.relayout_rank,
+                       max_chunk_bytes=w.max_chunk_bytes, with_backward=True)
+    step.qkv.copy_(normal_bf16(step.qkv.shape, seed=w.seed + 200, device="cuda"))
+    step.x.copy_(normal_bf16(step.x.shape, seed=w.seed + 201, device="cuda"))
+    for i, t in enumerate((step.shift, step.ada_scale, step.gate)):
+        t.copy_(normal_bf16(t.shape, seed=w.seed + 202 + i, std=0.1, device="cuda"))
+    step.grad_out.copy_(normal_bf16(step.grad_out.shape, seed=w.seed + 205, device="cuda"))
+    step.run()
+    step.backward()
+    torch.cuda.synchronize()
+    eager = {name_: t.detach().view(torch.int16).clone() for name_, t in _grads(step)}
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.backward()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for _, t in _grads(step):
+            t.zero_()                                  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {name_: t.detach().view(torch.int16).clone() for name_, t in _grads(step)}
+        _assert_same(got, eager, f"{name} backward replay {r}")
+    del graph
