@@ -142,3 +142,44 @@ def test_graph_replays_backward_match_eager(name):
         got = {name_: t.detach().view(torch.int16).clone() for name_, t in _grads(step)}
         _assert_same(got, eager, f"{name} backward replay {r}")
     del graph
+
+
+@pytest.mark.parametrize("name", ["tiny512", "8k_p6"])
+def test_graph_replays_token_sharded_ops_match_eager(name):
+    """The gated AdaLN chain over every rank interval, the ragged reduce-scatter
+    with the bias and the ragged row gather, captured once and replayed."""
+    import ulysses_layout_amd as h3
+    w = WORKLOADS[name]
+    say("graph token-sharded ops", name)
+    step = _step(w)
+    _fill_inputs(step, w.seed + 300)
+    n, c = step.n_tokens, step.channels
+    resid, y = torch.empty_like(step.x), torch.empty_like(step.x)
+    partials = [normal_bf16((n, c), seed=w.seed + 310 + j, device="cuda") for j in range(w.world)]
+    bias = normal_bf16((c,), seed=w.seed + 309, device="cuda")
+    shards = [torch.empty((cnt, c), dtype=torch.bfloat16, device="cuda") for _, cnt in step.tokens]
+    gathered = torch.empty((n, c), dtype=torch.bfloat16, device="cuda")
+    outs = [("resid", resid), ("y", y), ("gathered", gathered)] + [(f"shard{j}", t) for j, t in enumerate(shards)]
+
+    def ops():
+        for a, cnt in step.tokens:
+            h3.adaln_gate_modulate(step.x[a:a + cnt], step.branch[a:a + cnt], step.gate, step.shift,
+                                   step.ada_scale, resid[a:a + cnt], y[a:a + cnt], a, a + cnt, step.cu, step.eps)
+        h3.reduce_scatter(partials, bias, shards)
+        h3.gather_rows(shards, gathered)
+
+    ops()
+    torch.cuda.synchronize()
+    eager = {k: t.detach().view(torch.int16).clone() for k, t in outs}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for _, t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _assert_same({k: t.detach().view(torch.int16).clone() for k, t in outs}, eager, f"{name} ops replay {r}")
+    del graph
