@@ -32,6 +32,12 @@
  *   a kernel needs it, is a caller-owned workspace); work is enqueued on
  *   `stream` (a hipStream_t passed as void*, NULL = the default stream) and
  *   runs asynchronously.  Buffers must stay alive until that work completes.
+ * - Alignment: every device pointer handed to an entry point starts on a
+ *   16-byte boundary (the kernels move data in 16-byte vectors), except the
+ *   fp32 row log-sum-exp, which needs 4 bytes.  A misaligned pointer is
+ *   rejected with H3_ERR_ARG before anything is enqueued.  Whole allocations
+ *   of the HIP runtime and of torch always qualify; a view at an element
+ *   offset may not.
  * - Independent storage ([PR], Problem and behavior): no output may overlap
  *   an input or another output; overlap is detected on the host from the
  *   address ranges and rejected with H3_ERR_ALIAS.
@@ -240,10 +246,10 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
 /* ------------------------------------------------------------------------
  * h3_adaln_segment -- per-segment AdaLN on one rank's token interval.
  *
- * [DIST] Partition Contract: segment boundaries are clipped to the rank's
- * token interval [tok_begin, tok_end) and rebased before AdaLN modulation
- * and residual gating.  Local row i is global token tok_begin + i and takes
- * the parameter row of its GLOBAL segment s.
+ * [DIST] Partition Contract (the segment table of a token-sharded rank):
+ * local row i is global token tok_begin + i; every segment [cu[s], cu[s+1])
+ * is intersected with [tok_begin, tok_end) and shifted by -tok_begin, and
+ * row i takes the parameter row of its GLOBAL segment s.
  *   mode H3_ADALN_MODULATE:      y = (x - mean)/sqrt(var + eps) * (1 + scale[s]) + shift[s]
  *                                 (mean and biased var over the C channels, fp32)
  *   mode H3_ADALN_GATE_RESIDUAL: y = x + gate[s] * branch
@@ -310,8 +316,7 @@ h3_status h3_adaln_gate_modulate(const void *x, const void *branch, const void *
  *      and may be NULL otherwise.  Outputs must not overlap any input or
  *      each other.
  * world: P, 1..min(n_tokens, 64) (an empty part is H3_ERR_EMPTY_PARTITION).
- * channels: C, a multiple of 8, <= H3_MAX_CHANNELS; every pointer 16-byte
- *      aligned.  Launches: 1.
+ * channels: C, a multiple of 8, <= H3_MAX_CHANNELS.  Launches: 1.
  * ------------------------------------------------------------------------ */
 h3_status h3_reduce_scatter(const void *const *partials, const void *bias, void *const *out,
                             int64_t n_tokens, int32_t channels, int32_t world, int32_t rank,

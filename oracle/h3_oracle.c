@@ -381,9 +381,9 @@ int h3o_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 /* ------------------------------------------------------------------------ */
 /* Per-segment AdaLN modulation and residual gating on one token interval.  */
 /*                                                                          */
-/* Source: "Distributed H3 Execution", Partition Contract -- segment        */
-/* boundaries are clipped to the rank's token interval and rebased before   */
-/* AdaLN modulation and residual gating.  The clipped, rebased table is     */
+/* Source: "Distributed H3 Execution", Partition Contract -- a token-       */
+/* sharded rank's local row i is global token a + i, and each segment is    */
+/* intersected with [a, b) and shifted by -a for these ops.  That table is  */
 /* computed by the caller (oracle.clip_segments) and passed in as           */
 /* (seg_id[e], local_begin[e], local_end[e]).  The pages name the two ops   */
 /* but do not write them out; the reading taken is the usual DiT form:      */

@@ -133,9 +133,10 @@ def partition(total: int, parts: int) -> List[Tuple[int, int]]:
 def clip_segments(cu: Sequence[int], a: int, b: int) -> List[Tuple[int, int, int]]:
     """Clip the global segment table to the token interval ``[a, b)`` and rebase it.
 
-    "Distributed H3 Execution", Partition Contract: segment boundaries are
-    clipped to each rank's token interval and rebased before AdaLN modulation
-    and residual gating.  ``cu`` holds the global offsets ``cu[0]=0 < ... <
+    "Distributed H3 Execution", Partition Contract (the table a token-sharded
+    rank's AdaLN ops use): local row ``i`` is global token ``a + i``, and each
+    segment is intersected with ``[a, b)`` and shifted by ``-a``.  ``cu``
+    holds the global offsets ``cu[0]=0 < ... <
     cu[S]=N``.  Returns ``(s, lo - a, hi - a)`` for every global segment ``s``
     whose clipped part ``[lo, hi) = [max(cu[s], a), min(cu[s+1], b))`` is not
     empty; ``s`` stays the GLOBAL segment id.

@@ -250,7 +250,7 @@ def _attn(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), g=None, o=FAKE + (3 <<
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), ARG), (dict(o=None), ARG), (dict(d=64), UNSUP), (dict(h=0), EMPTY), (dict(n=0), EMPTY),
     (dict(cu=(0, 96, 96, 512)), SEGS), (dict(cu=(1, 96, 512)), SEGS), (dict(cu=(0, 96, 500)), SEGS),
-    (dict(scale=0.0), ARG), (dict(scale=float("nan")), ARG), (dict(o=FAKE + 100), ALIAS),
+    (dict(scale=0.0), ARG), (dict(scale=float("nan")), ARG), (dict(o=FAKE + 256), ALIAS),
     (dict(g=FAKE + (3 << 32) + 64), ALIAS), (dict(cu=tuple(range(0, 2 * 300, 2)) + (600,), n=600), SEGS),
 ])
 @fake_addresses
@@ -273,7 +273,7 @@ def _adaln(mode=0, x=FAKE, b=None, shift=FAKE + (1 << 32), scale=FAKE + (2 << 32
     (dict(mode=2), ARG), (dict(x=None), ARG), (dict(shift=None), ARG), (dict(mode=1), ARG),
     (dict(a=10, e=10), EMPTY), (dict(a=-1), EMPTY), (dict(c=7170), UNSUP), (dict(c=0), UNSUP),
     (dict(c=16392), UNSUP), (dict(e=600), SEGS), (dict(cu=(0, 300, 200, 512)), SEGS),
-    (dict(y=FAKE + 1000), ALIAS), (dict(eps=float("nan")), ARG),
+    (dict(y=FAKE + 1024), ALIAS), (dict(eps=float("nan")), ARG),
 ])
 @fake_addresses
 def test_adaln_rejects(kw, status):
@@ -369,3 +369,172 @@ def test_gather_rows_rejects(kw, status):
     rc, info = _gather(**kw)
     assert rc == status, LIB.h3_last_error()
     assert info.launches == 0
+
+
+# ---------------------------------------------------------------------------
+# alignment: every device pointer a kernel reads or writes in 16-byte vectors
+# is refused when it does not start on a 16-byte boundary (the fp32 lse on a
+# 4-byte one), before anything is enqueued
+# ---------------------------------------------------------------------------
+
+MIS = 2          # one bf16 element past an aligned address
+
+
+def _h2s(layout, dst=FAKE, src=None):
+    p = layout.world
+    if src is None:
+        src = [FAKE * 2 + j * (1 << 28) for j in range(p)]
+    arr = (ctypes.c_void_p * max(len(src), 1))(*src)
+    info = _PlanInfo()
+    return LIB.h3_head2seq(ctypes.byref(layout), arr, dst, None, ctypes.byref(info)), info
+
+
+def _six(i=None):
+    """Six well-separated fake destination pointers, entry i misaligned."""
+    out = [FAKE * 2 + j * (1 << 28) for j in range(6)]
+    if i is not None:
+        out[i] += MIS
+    return out
+
+
+@fake_addresses
+@pytest.mark.parametrize("case", ["src", "dst0", "dst5"])
+def test_seq2head_rejects_misaligned(case):
+    lay = _layout()
+    if case == "src":
+        rc, info = _seq2head(lay, src=FAKE + MIS, dst=_six())
+    else:
+        rc, info = _seq2head(lay, dst=_six(int(case[3:])))
+    assert rc == ARG, LIB.h3_last_error()
+    assert "aligned" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("case", ["dst", "src1"])
+def test_head2seq_rejects_misaligned(case):
+    lay = _layout(n_planes=1)
+    if case == "dst":
+        rc, info = _h2s(lay, dst=FAKE + MIS)
+    else:
+        rc, info = _h2s(lay, src=[FAKE * 2, FAKE * 2 + (1 << 28) + MIS])
+    assert rc == ARG, LIB.h3_last_error()
+    assert "aligned" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("case", ["grad_src", "grad_dst2"])
+def test_seq2head_backward_rejects_misaligned(case):
+    lay = _layout()
+    if case == "grad_src":
+        rc, info = _seq2head_bwd(lay, grad_src=FAKE + 8, grad_dst=_six())
+    else:
+        rc, info = _seq2head_bwd(lay, grad_dst=_six(2))
+    assert rc == ARG, LIB.h3_last_error()
+    assert "aligned" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("case", ["grad_dst", "grad_src0"])
+def test_head2seq_backward_rejects_misaligned(case):
+    lay = _layout(n_planes=1)
+    if case == "grad_dst":
+        rc, info = _head2seq_bwd(lay, grad_dst=FAKE + MIS)
+    else:
+        rc, info = _head2seq_bwd(lay, grad_src=[FAKE * 2 + 4, FAKE * 2 + (1 << 28)])
+    assert rc == ARG, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "o"])
+def test_packed_attn_rejects_misaligned(name):
+    kw = dict(g=FAKE + (4 << 32))
+    kw[name] = (kw.get(name) or dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), o=FAKE + (3 << 32))[name]) + MIS
+    rc, info = _attn(**kw)
+    assert rc == ARG, LIB.h3_last_error()
+    assert name in LIB.h3_last_error().decode() and "aligned" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+def _attn_lse(lse, n=512, h=4, cu=(0, 96, 256, 512)):
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_packed_attn_lse(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), None, FAKE + (3 << 32), lse, n, h, 128,
+                                cua, len(cu) - 1, 0.088, None, ctypes.byref(info))
+    return rc, info
+
+
+@fake_addresses
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_packed_attn_lse_rejects_misaligned(off):
+    rc, info = _attn_lse(FAKE + (5 << 32) + off)
+    assert rc == ARG, LIB.h3_last_error()
+    assert "lse" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+BWD_NAMES = ["q", "k", "v", "g", "o", "dout", "lse", "dq", "dk", "dv", "dg", "workspace"]
+
+
+def _attn_bwd(mis=None, off=MIS, n=512, h=4, cu=(0, 96, 256, 512)):
+    ptr = {name: FAKE + (i << 32) for i, name in enumerate(BWD_NAMES)}
+    if mis is not None:
+        ptr[mis] += off
+    ws = LIB.h3_packed_attn_backward_workspace(n, h, 1)
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_packed_attn_backward(*[ptr[x] for x in BWD_NAMES], ws, n, h, 128, cua, len(cu) - 1, 0.088, None,
+                                     ctypes.byref(info))
+    return rc, info
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", BWD_NAMES)
+def test_packed_attn_backward_rejects_misaligned(name):
+    rc, info = _attn_bwd(name)
+    assert rc == ARG, LIB.h3_last_error()
+    assert name in LIB.h3_last_error().decode() and "aligned" in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", ["x", "shift", "scale", "y"])
+def test_adaln_modulate_rejects_misaligned(name):
+    kw = dict(x=FAKE, shift=FAKE + (1 << 32), scale=FAKE + (2 << 32), y=FAKE + (3 << 32))
+    kw[name] += MIS
+    rc, info = _adaln(**kw)
+    assert rc == ARG, LIB.h3_last_error()
+    assert name in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", ["b", "gate"])
+def test_adaln_gate_rejects_misaligned(name):
+    kw = dict(mode=1, shift=None, scale=None, b=FAKE + (4 << 32), gate=FAKE + (5 << 32))
+    kw[name] += 8
+    rc, info = _adaln(**kw)
+    assert rc == ARG, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", ["x", "b", "gate", "shift", "scale", "resid", "y"])
+def test_adaln_gate_modulate_rejects_misaligned(name):
+    base = dict(x=FAKE, b=FAKE + (1 << 32), gate=FAKE + (2 << 32), shift=FAKE + (3 << 32), scale=FAKE + (4 << 32),
+                resid=FAKE + (5 << 32), y=FAKE + (6 << 32))
+    base[name] += MIS
+    rc, info = _chain(**base)
+    assert rc == ARG, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+@fake_addresses
+def test_misaligned_call_leaves_no_state():
+    rc, _ = _attn(q=FAKE + MIS)
+    assert rc == ARG
+    assert h3.partition(56, 6, 0) == (0, 10)
+    assert LIB.h3_last_error().decode() == ""

@@ -1,10 +1,10 @@
 // adaln.hip -- per-segment AdaLN modulation and residual gating on one token
-// interval ("Distributed H3 Execution", Partition Contract: the segment table
-// is clipped to the rank's token interval and rebased before these ops), and
-// the two chained: one sub-block's gated residual, modulated at once by the
-// next sub-block's parameters, so x and the branch are read once and the
-// residual never has to be read back (the modulation takes the fp32 residual
-// from registers; only the stored copy is rounded to bf16).
+// interval ("Distributed H3 Execution", Partition Contract: local row i is
+// global token a + i, each segment intersected with [a, b) and shifted by
+// -a), and the two chained: one sub-block's gated residual, modulated at once
+// by the next sub-block's parameters, so x and the branch are read once and
+// the residual never has to be read back (the modulation takes the fp32
+// residual from registers; only the stored copy is rounded to bf16).
 //
 // One wave64 owns one row of C channels.  When C is a multiple of 512 (H3:
 // 7168 = 14 x 512) every lane owns exactly C/512 16-byte vectors of the row:

@@ -80,6 +80,15 @@ h3_status check_segments(const int64_t *cu, int32_t n_segments, int64_t n_tokens
     return H3_OK;
 }
 
+// Every kernel moves bf16 data in 16-byte vectors (and fp32 row terms in
+// 4-byte words), so a buffer must start on that boundary.  NULL passes: the
+// callers check presence separately.
+h3_status check_aligned(const void *p, const char *what, int index, unsigned align = 16) {
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+        return fail(H3_ERR_ARG, "%s[%d] = %p is not %u-byte aligned", what, index, p, align);
+    return H3_OK;
+}
+
 void clear_info(h3_plan_info *info) {
     if (info) std::memset(info, 0, sizeof *info);
 }
@@ -197,6 +206,7 @@ h3_status h3_seq2head(const h3_layout *L, const void *src, void *const *dst, voi
     if (st != H3_OK) return st;
     if (!src) return fail(H3_ERR_ARG, "src is NULL");
     if (!dst) return fail(H3_ERR_ARG, "dst is NULL");
+    if ((st = check_aligned(src, "src", 0)) != H3_OK) return st;
     const int P = L->world, K = L->n_planes;
     const int r0 = L->rank < 0 ? 0 : L->rank;
     const int nr = L->rank < 0 ? P : 1;
@@ -209,6 +219,7 @@ h3_status h3_seq2head(const h3_layout *L, const void *src, void *const *dst, voi
     for (int j = r0; j < r0 + nr; ++j)
         for (int p = 0; p < K; ++p) {
             if (!dst[j * K + p]) return fail(H3_ERR_ARG, "dst[%d] (rank %d, plane %d) is NULL", j * K + p, j, p);
+            if ((st = check_aligned(dst[j * K + p], "dst", j * K + p)) != H3_OK) return st;
             outs.push_back(range_of(dst[j * K + p], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "dst",
                                     j * K + p));
         }
@@ -273,6 +284,7 @@ h3_status h3_head2seq(const h3_layout *L, const void *const *src, void *dst, voi
     if (st != H3_OK) return st;
     if (!src) return fail(H3_ERR_ARG, "src is NULL");
     if (!dst) return fail(H3_ERR_ARG, "dst is NULL");
+    if ((st = check_aligned(dst, "dst", 0)) != H3_OK) return st;
     const int P = L->world;
     const int r0 = L->rank < 0 ? 0 : L->rank;
     const int nr = L->rank < 0 ? P : 1;
@@ -283,6 +295,7 @@ h3_status h3_head2seq(const h3_layout *L, const void *const *src, void *dst, voi
     std::vector<Range> ins, outs{range_of(dst, (uint64_t)L->n_tokens * row_bytes, "dst", 0)};
     for (int j = r0; j < r0 + nr; ++j) {
         if (!src[j]) return fail(H3_ERR_ARG, "src[%d] is NULL", j);
+        if ((st = check_aligned(src[j], "src", j)) != H3_OK) return st;
         ins.push_back(range_of(src[j], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "src", j));
     }
     if ((st = check_alias(ins, outs)) != H3_OK) return st;
@@ -346,6 +359,7 @@ h3_status h3_seq2head_backward(const h3_layout *L, const void *const *grad_dst, 
     if (st != H3_OK) return st;
     if (!grad_dst) return fail(H3_ERR_ARG, "grad_dst is NULL");
     if (!grad_src) return fail(H3_ERR_ARG, "grad_src is NULL");
+    if ((st = check_aligned(grad_src, "grad_src", 0)) != H3_OK) return st;
     const int P = L->world, K = L->n_planes;
     const int r0 = L->rank < 0 ? 0 : L->rank;
     const int nr = L->rank < 0 ? P : 1;
@@ -358,6 +372,7 @@ h3_status h3_seq2head_backward(const h3_layout *L, const void *const *grad_dst, 
         for (int p = 0; p < K; ++p) {
             if (!grad_dst[j * K + p])
                 return fail(H3_ERR_ARG, "grad_dst[%d] (rank %d, plane %d) is NULL", j * K + p, j, p);
+            if ((st = check_aligned(grad_dst[j * K + p], "grad_dst", j * K + p)) != H3_OK) return st;
             ins.push_back(range_of(grad_dst[j * K + p], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "grad_dst",
                                    j * K + p));
         }
@@ -426,6 +441,7 @@ h3_status h3_head2seq_backward(const h3_layout *L, const void *grad_dst, void *c
     if (st != H3_OK) return st;
     if (!grad_dst) return fail(H3_ERR_ARG, "grad_dst is NULL");
     if (!grad_src) return fail(H3_ERR_ARG, "grad_src is NULL");
+    if ((st = check_aligned(grad_dst, "grad_dst", 0)) != H3_OK) return st;
     const int P = L->world;
     const int r0 = L->rank < 0 ? 0 : L->rank;
     const int nr = L->rank < 0 ? P : 1;
@@ -436,6 +452,7 @@ h3_status h3_head2seq_backward(const h3_layout *L, const void *grad_dst, void *c
     std::vector<Range> ins{range_of(grad_dst, (uint64_t)L->n_tokens * row_bytes, "grad_dst", 0)}, outs;
     for (int j = r0; j < r0 + nr; ++j) {
         if (!grad_src[j]) return fail(H3_ERR_ARG, "grad_src[%d] is NULL", j);
+        if ((st = check_aligned(grad_src[j], "grad_src", j)) != H3_OK) return st;
         outs.push_back(range_of(grad_src[j], (uint64_t)L->n_tokens * hn[j] * L->head_dim * 2, "grad_src", j));
     }
     if ((st = check_alias(ins, outs)) != H3_OK) return st;
@@ -506,6 +523,13 @@ static h3_status packed_attn_impl(const void *q, const void *k, const void *v, c
         return fail(H3_ERR_ARG, "scale must be a positive finite number");
     h3_status st = check_segments(cu, n_segments, n_tokens, true);
     if (st != H3_OK) return st;
+    {
+        const void *vec[] = {q, k, v, g, o};
+        const char *names[] = {"q", "k", "v", "g", "o"};
+        for (int i = 0; i < 5; ++i)
+            if ((st = check_aligned(vec[i], names[i], 0)) != H3_OK) return st;
+        if ((st = check_aligned(lse, "lse", 0, 4)) != H3_OK) return st;
+    }
     const uint64_t bytes = (uint64_t)n_tokens * n_heads * head_dim * 2;
     std::vector<Range> ins{range_of(q, bytes, "q", 0), range_of(k, bytes, "k", 0), range_of(v, bytes, "v", 0)};
     if (g) ins.push_back(range_of(g, bytes, "g", 0));
@@ -598,6 +622,13 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
         return fail(H3_ERR_ARG, "scale must be a positive finite number");
     h3_status st = check_segments(cu, n_segments, n_tokens, true);
     if (st != H3_OK) return st;
+    {
+        const void *vec[] = {q, k, v, g, o, dout, dq, dk, dv, dg, workspace};
+        const char *names[] = {"q", "k", "v", "g", "o", "dout", "dq", "dk", "dv", "dg", "workspace"};
+        for (int i = 0; i < 11; ++i)
+            if ((st = check_aligned(vec[i], names[i], 0)) != H3_OK) return st;
+        if ((st = check_aligned(lse, "lse", 0, 4)) != H3_OK) return st;
+    }
     const int64_t rows = n_tokens * n_heads;
     if ((uint64_t)rows > UINT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens * n_heads exceeds 2^32-1");
     const int64_t need = h3_packed_attn_backward_workspace(n_tokens, n_heads, g != nullptr);
@@ -668,13 +699,6 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
         info->bytes_written = (int64_t)(bytes * (g ? 4 : 3));
     }
     return ok();
-}
-
-// 16-byte vector accesses need 16-byte aligned buffers.
-static h3_status check_aligned(const void *p, const char *what, int index) {
-    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-        return fail(H3_ERR_ARG, "%s[%d] is not 16-byte aligned", what, index);
-    return H3_OK;
 }
 
 // Shared checks of the ragged collectives: token split, channels, index range.
@@ -823,6 +847,12 @@ static h3_status adaln_impl(int32_t mode, const void *x, const void *branch, con
     if (modulate && !(eps >= 0.f && eps < 1e30f)) return fail(H3_ERR_ARG, "eps must be a finite number >= 0");
     h3_status st = check_segments(cu, n_segments, tok_end, false);
     if (st != H3_OK) return st;
+    {
+        const void *vec[] = {x, branch, shift, scale, gate, resid, y};
+        const char *names[] = {"x", "branch", "shift", "scale", "gate", "resid", "y"};
+        for (int i = 0; i < 7; ++i)
+            if ((st = check_aligned(vec[i], names[i], 0)) != H3_OK) return st;
+    }
 
     const int64_t n_rows = tok_end - tok_begin;
     const uint64_t row_bytes = (uint64_t)channels * 2;
