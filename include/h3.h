@@ -90,9 +90,12 @@ typedef struct h3_layout {
     int32_t world;           /* P: virtual ranks, 1 <= P <= min(H, N)                          */
     int32_t rank;            /* -1: every rank; 0..P-1: only that rank's share                */
     int32_t reserved;        /* must be 0                                                     */
-    int64_t max_chunk_bytes; /* 0: one launch per plane; > 0: each launch covers at most
-                                floor(max_chunk_bytes / (H*D*2)) tokens of one plane (the
-                                896,000,000-byte window of [PR] gives 62,500 tokens)          */
+    int64_t max_chunk_bytes; /* 0: one launch per plane; > 0: no launch reads more than
+                                this many source bytes.  A launch moves, per token of one
+                                plane, B = (selected heads)*D*2 bytes (H*D*2 for rank -1,
+                                H_j*D*2 for rank j), so it covers floor(max_chunk_bytes / B)
+                                tokens.  The 896,000,000-byte window of [PR] gives 62,500
+                                tokens of a whole 56-head plane.  Below B: H3_ERR_ARG      */
 } h3_layout;
 
 typedef struct h3_plan_info {

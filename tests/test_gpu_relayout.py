@@ -43,8 +43,14 @@ def test_seq2head_small(n, k, world, rank, chunk_rows):
     for j in ranks:
         for p in range(k):
             assert np.array_equal(to_bits(bufs[j][p]), ref[(j, p)]), (j, p)
-    chunks = 1 if chunk_rows == 0 else -(-n // chunk_rows)
+    # the cap bounds a launch's source bytes: per token it moves the selected ranks' heads
+    sel_bytes = sum(heads[j][1] for j in ranks) * 128 * 2
+    chunk_tok = n if chunk_rows == 0 else min(n, chunk_rows * 56 * 128 * 2 // sel_bytes)
+    chunks = -(-n // chunk_tok)
     assert info.chunks == chunks and info.launches == k * chunks
+    assert info.chunk_tokens == chunk_tok
+    if chunk_rows:
+        assert info.max_launch_src_bytes <= chunk_rows * 56 * 128 * 2
     assert np.array_equal(to_bits(src), src_bits)          # the source is untouched
 
 
@@ -117,24 +123,55 @@ def test_seq2head_workload_full(name):
 
 
 def test_chunked_plan_and_negative_control():
-    """The bounded-window plan runs at 250k (launch sizes asserted), and the same
-    assertion fails for the unchunked plan; both give identical bits."""
+    """The bounded-window plan at 250k: with the 896,000,000-byte cap no launch
+    reads more than the window (every rank: 62,500-token chunks of whole
+    planes; rank 0's 7-head share: one launch per plane, 448,000,000 bytes),
+    and the same assertion fails for the uncapped every-rank plan.  All plans
+    give identical bits."""
     h3 = _h3()
     w = WORKLOADS["250k_p8_qkvg"]
     say("chunk control 250k")
     src = _workload_src(w)
     heads = h3.head_split(56, w.world)
-    chunked = _alloc_rank_bufs(w.n_tokens, heads, w.planes, [0])
-    whole = _alloc_rank_bufs(w.n_tokens, heads, w.planes, [0])
     window = 896_000_000
-    info_c = h3.seq2head(src, chunked, w.world, rank=0, max_chunk_bytes=window)
-    info_w = h3.seq2head(src, whole, w.world, rank=0, max_chunk_bytes=0)
+    chunked = _alloc_rank_bufs(w.n_tokens, heads, w.planes, range(w.world))
+    info_c = h3.seq2head(src, chunked, w.world, max_chunk_bytes=window)
     torch.cuda.synchronize()
     assert info_c.chunk_tokens == 62500 and info_c.chunks == 4 and info_c.launches == 16
-    assert info_c.chunk_tokens * 56 * 128 * 2 <= window
-    assert info_w.chunks == 1 and info_w.chunk_tokens * 56 * 128 * 2 > window   # negative control
+    assert info_c.max_launch_src_bytes == window
+    whole = _alloc_rank_bufs(w.n_tokens, heads, w.planes, range(w.world))
+    info_w = h3.seq2head(src, whole, w.world, max_chunk_bytes=0)
+    torch.cuda.synchronize()
+    assert info_w.chunks == 1 and info_w.max_launch_src_bytes > window     # negative control
+    for j in range(w.world):
+        for p in range(w.planes):
+            assert torch.equal(chunked[j][p].view(torch.int16), whole[j][p].view(torch.int16)), (j, p)
+    del whole
+    share = _alloc_rank_bufs(w.n_tokens, heads, w.planes, [0])
+    info_r = h3.seq2head(src, share, w.world, rank=0, max_chunk_bytes=window)
+    torch.cuda.synchronize()
+    assert info_r.chunks == 1 and info_r.launches == w.planes
+    assert info_r.max_launch_src_bytes == w.n_tokens * heads[0][1] * 128 * 2 <= window
     for p in range(w.planes):
-        assert torch.equal(chunked[0][p].view(torch.int16), whole[0][p].view(torch.int16))
+        assert torch.equal(share[0][p].view(torch.int16), chunked[0][p].view(torch.int16)), p
+
+
+def test_rank_share_cap_of_one_token():
+    """A cap of exactly one token of the selected rank's heads is legal and gives
+    one-token launches with the same bits."""
+    h3 = _h3()
+    n, world, rank = 37, 6, 4
+    say("one-token cap", n, world, rank)
+    src_bits = normal_bf16_bits((n, 3, 56, 128), seed=71)
+    src = to_device(src_bits)
+    heads = h3.head_split(56, world)
+    bufs = _alloc_rank_bufs(n, heads, 3, [rank])
+    info = h3.seq2head(src, bufs, world, rank=rank, max_chunk_bytes=heads[rank][1] * 128 * 2)
+    torch.cuda.synchronize()
+    assert info.chunk_tokens == 1 and info.chunks == n and info.launches == 3 * n
+    ref = oracle.seq2head(src_bits, world, ranks=[rank])
+    for p in range(3):
+        assert np.array_equal(to_bits(bufs[rank][p]), ref[(rank, p)]), p
 
 
 @pytest.mark.parametrize("name", ["128k_p4_qkvg", "250k_p8_qkvg"])

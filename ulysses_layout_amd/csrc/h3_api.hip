@@ -93,6 +93,15 @@ void clear_info(h3_plan_info *info) {
     if (info) std::memset(info, 0, sizeof *info);
 }
 
+// Bytes of one plane that a relayout launch moves per token: the heads of
+// every selected rank (a valid layout is assumed).
+int64_t selected_token_bytes(const h3_layout *L) {
+    if (L->rank < 0) return (int64_t)L->n_heads * L->head_dim * 2;
+    int64_t hb, hn;
+    split(L->n_heads, L->world, L->rank, &hb, &hn);
+    return hn * L->head_dim * 2;
+}
+
 // Shared validation of a relayout contract.
 h3_status check_layout(const h3_layout *L, bool head2seq) {
     if (!L) return fail(H3_ERR_ARG, "layout is NULL");
@@ -117,18 +126,21 @@ h3_status check_layout(const h3_layout *L, bool head2seq) {
         return fail(H3_ERR_ARG, "rank = %d; legal values are -1 (every rank) or 0..%d", L->rank, L->world - 1);
     if (L->max_chunk_bytes < 0)
         return fail(H3_ERR_ARG, "max_chunk_bytes = %lld must be >= 0", (long long)L->max_chunk_bytes);
-    const int64_t row_bytes = (int64_t)L->n_heads * L->head_dim * 2;
-    if (L->max_chunk_bytes > 0 && L->max_chunk_bytes < row_bytes)
-        return fail(H3_ERR_ARG, "max_chunk_bytes = %lld is below one token row of one plane (%lld bytes)",
-                    (long long)L->max_chunk_bytes, (long long)row_bytes);
+    const int64_t tok_bytes = selected_token_bytes(L);
+    if (L->max_chunk_bytes > 0 && L->max_chunk_bytes < tok_bytes)
+        return fail(H3_ERR_ARG, "max_chunk_bytes = %lld is below what one token of one plane moves for the "
+                    "selected ranks (%lld bytes)", (long long)L->max_chunk_bytes, (long long)tok_bytes);
     return H3_OK;
 }
 
-// Token chunking of one plane: user cap, then the 32-bit index range of the kernel.
+// Token chunking of one plane.  The cap bounds the source bytes one launch
+// reads: a launch moves, per token, the selected ranks' heads of one plane
+// (every head for rank = -1, H_j heads for rank j's share), so a chunk holds
+// floor(cap / those bytes) tokens.  Then the 32-bit index range of the kernel.
 void plan_chunks(const h3_layout *L, uint32_t packed_stride_vec, int64_t *chunk_tokens, int32_t *n_chunks,
                  int64_t *user_chunk) {
-    const int64_t row_bytes = (int64_t)L->n_heads * L->head_dim * 2;
-    int64_t c = L->max_chunk_bytes > 0 ? L->max_chunk_bytes / row_bytes : L->n_tokens;
+    const int64_t tok_bytes = selected_token_bytes(L);
+    int64_t c = L->max_chunk_bytes > 0 ? L->max_chunk_bytes / tok_bytes : L->n_tokens;
     c = std::min<int64_t>(c, L->n_tokens);
     *user_chunk = c;
     // keep t*stride + run and tokens*run below 2^31 inside one launch
