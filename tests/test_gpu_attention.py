@@ -189,3 +189,29 @@ def test_attention_workload_sampled_rows(name):
     compare(got, ref, f"{name} sampled {len(rows)} rows")
     expected_flops = 4 * 128 * c * sum(L * L for L in w.segment_lengths)
     assert info.flops == expected_flops
+
+
+@pytest.mark.timeout(900)
+def test_attention_32k_every_row():
+    """The 32k workload (four 8192-token segments, one rank's 14 heads, QKV) in
+    the bench's launch configuration, every row of every head against the fp64
+    oracle: 1.9e12 oracle FLOPs, about a minute on 16 host cores."""
+    h3 = _h3()
+    w = WORKLOADS["32k_p4"]
+    j = w.attn_rank
+    heads = h3.head_split(56, w.world)
+    n, c = w.n_tokens, heads[j][1]
+    say("attention 32k every row", "rank", j, "heads", c, "oracle threads", oracle.default_threads())
+    ops = [normal_bf16((n, c, 128), seed=w.seed + 10 + p, device="cuda") for p in range(3)]
+    o, info = _run(ops[0], ops[1], ops[2], None, w.cu)
+    assert info.flops == 4 * 128 * c * sum(L * L for L in w.segment_lengths)
+    bits = [to_bits(t) for t in ops]
+    got = to_bits(o)
+    del ops, o
+    ref = oracle.attention_rows(bits[0], bits[1], bits[2], None, w.cu, SCALE)
+    assert ref.shape == (n, c, 128)
+    compare(got, ref, f"32k every row ({n} rows x {c} heads)")
+    # the per-segment errors as well, so that no segment hides behind the others
+    for s in range(len(w.cu) - 1):
+        a, b = w.cu[s], w.cu[s + 1]
+        compare(got[a:b], ref[a:b], f"32k segment {s}")
