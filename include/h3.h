@@ -247,6 +247,36 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
                                   void *stream, h3_plan_info *info);
 
 /* ------------------------------------------------------------------------
+ * h3_packed_attn_backward_noalloc -- h3_packed_attn_backward for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace; its
+ * scratch (the row terms D and, gated, e = dout * sig(g)) lives in a
+ * library-owned device array of H3_NOALLOC_SCRATCH_BYTES bytes, one per GPU
+ * the library runs on, created with the code object and held until the
+ * process ends.  The call allocates and frees nothing.
+ *
+ * Arguments, results (bit for bit those of h3_packed_attn_backward on the
+ * same inputs), launches and errors as h3_packed_attn_backward, minus the
+ * workspace.  Scratch needed, h3_packed_attn_backward_workspace(N, H,
+ * g != NULL), above H3_NOALLOC_SCRATCH_BYTES is rejected with
+ * H3_ERR_UNSUPPORTED before anything is enqueued (64 MiB: e.g. 8192 tokens
+ * x 28 heads gated, or any ungated size up to 16M token-head rows).
+ * The array's contents are unspecified on entry and nothing in it has to
+ * start at zero.  Every call on one GPU uses that GPU's one array: two
+ * calls whose work may overlap in time on the same GPU (different streams,
+ * or threads without ordering) race on it and give undefined results;
+ * calls ordered on one stream are safe.  The stream must belong to the
+ * current device.
+ * ------------------------------------------------------------------------ */
+#define H3_NOALLOC_SCRATCH_BYTES (64ll << 20)
+h3_status h3_packed_attn_backward_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                          const void *o, const void *dout, const float *lse,
+                                          void *dq, void *dk, void *dv, void *dg,
+                                          int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                          const int64_t *cu_seqlens, int32_t n_segments, float scale,
+                                          void *stream, h3_plan_info *info);
+
+/* ------------------------------------------------------------------------
  * h3_adaln_segment -- per-segment AdaLN on one rank's token interval.
  *
  * [DIST] Partition Contract (the segment table of a token-sharded rank):

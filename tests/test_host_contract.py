@@ -538,3 +538,69 @@ def test_misaligned_call_leaves_no_state():
     assert rc == ARG
     assert h3.partition(56, 6, 0) == (0, 10)
     assert LIB.h3_last_error().decode() == ""
+
+
+# ---------------------------------------------------------------------------
+# h3_packed_attn_backward_noalloc: every check runs before the scratch array
+# is looked up, so all rejections are visible without a GPU
+# ---------------------------------------------------------------------------
+
+NOALLOC_NAMES = ["q", "k", "v", "g", "o", "dout", "lse", "dq", "dk", "dv", "dg"]
+
+
+def _attn_bwd_noalloc(mis=None, off=MIS, null=None, n=512, h=4, cu=(0, 96, 256, 512), gated=True):
+    ptr = {name: FAKE + (i << 32) for i, name in enumerate(NOALLOC_NAMES)}
+    if not gated:
+        ptr["g"] = ptr["dg"] = None
+    if mis is not None:
+        ptr[mis] += off
+    if null is not None:
+        ptr[null] = None
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    info = _PlanInfo()
+    rc = LIB.h3_packed_attn_backward_noalloc(*[ptr[x] for x in NOALLOC_NAMES], n, h, 128, cua, len(cu) - 1, 0.088,
+                                             None, ctypes.byref(info))
+    return rc, info
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define H3_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == h3.NOALLOC_SCRATCH_BYTES
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", NOALLOC_NAMES)
+def test_noalloc_backward_rejects_misaligned(name):
+    rc, info = _attn_bwd_noalloc(mis=name)
+    assert rc == ARG, LIB.h3_last_error()
+    assert name in LIB.h3_last_error().decode()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("name", ["q", "lse", "dq", "dg"])
+def test_noalloc_backward_rejects_null(name):
+    rc, info = _attn_bwd_noalloc(null=name)
+    assert rc == ARG, LIB.h3_last_error()
+    assert info.launches == 0
+
+
+@fake_addresses
+@pytest.mark.parametrize("n,h,gated", [(16384, 16, True), (131072, 14, True), (1 << 21, 9, False)])
+def test_noalloc_backward_rejects_beyond_scratch(n, h, gated):
+    need = LIB.h3_packed_attn_backward_workspace(n, h, int(gated))
+    assert need > h3.NOALLOC_SCRATCH_BYTES
+    rc, info = _attn_bwd_noalloc(n=n, h=h, cu=(0, n), gated=gated)
+    assert rc == UNSUP, LIB.h3_last_error()
+    msg = LIB.h3_last_error().decode()
+    assert str(need) in msg and str(h3.NOALLOC_SCRATCH_BYTES) in msg
+    assert info.launches == 0
+
+
+@fake_addresses
+def test_noalloc_backward_rejects_alias_and_segments():
+    rc, _ = _attn_bwd_noalloc(cu=(0, 96, 96, 512))
+    assert rc == SEGS
+    rc, _ = _attn_bwd_noalloc(mis="dq", off=-(7 << 32) + 256)     # dq moved inside q
+    assert rc == ALIAS, LIB.h3_last_error()

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "h3_internal.h"
@@ -614,16 +615,54 @@ int64_t h3_packed_attn_backward_workspace(int64_t n_tokens, int32_t n_heads, int
     return bwd_delta_bytes(rows) + (gated ? rows * H3_HEAD_DIM * 2 : 0);
 }
 
-h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, const void *g, const void *o,
-                                  const void *dout, const float *lse, void *dq, void *dk, void *dv, void *dg,
-                                  void *workspace, int64_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
-                                  int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale, void *stream,
-                                  h3_plan_info *info) {
+}  // extern "C"
+
+// ---- the scratch array of the no-allocation backward ------------------------
+// One array per GPU that runs the library, held until the process ends.  Host
+// code never uses the name below as an address: each device's address comes
+// from hipGetSymbolAddress, taken once with that device current.
+static __device__ __align__(256) unsigned char scratch[H3_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's copy of `scratch` (looked up on the first call there).
+h3_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(H3_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(H3_ERR_UNSUPPORTED, "device %d: the no-allocation scratch serves devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(H3_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return H3_OK;
+}
+
+// The attention backward with a caller workspace, or (use_scratch) with the
+// current device's scratch array in its place.  Every argument check runs
+// before the scratch address is looked up or anything is enqueued.
+h3_status attn_backward_impl(const void *q, const void *k, const void *v, const void *g, const void *o,
+                             const void *dout, const float *lse, void *dq, void *dk, void *dv, void *dg,
+                             void *workspace, int64_t workspace_bytes, bool use_scratch, int64_t n_tokens,
+                             int32_t n_heads, int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale,
+                             void *stream, h3_plan_info *info) {
     clear_info(info);
     if (!q || !k || !v || !o || !dout || !lse) return fail(H3_ERR_ARG, "q, k, v, o, dout and lse must be non-NULL");
     if (!dq || !dk || !dv) return fail(H3_ERR_ARG, "dq, dk and dv must be non-NULL");
     if ((g == nullptr) != (dg == nullptr)) return fail(H3_ERR_ARG, "dg must be given exactly when g is");
-    if (!workspace) return fail(H3_ERR_ARG, "workspace is NULL");
+    if (!use_scratch && !workspace) return fail(H3_ERR_ARG, "workspace is NULL");
     if (n_tokens < 1) return fail(H3_ERR_EMPTY_PARTITION, "n_tokens = %lld: no tokens", (long long)n_tokens);
     if (n_tokens > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens = %lld exceeds 2^31-1", (long long)n_tokens);
     if (n_heads < 1 || n_heads > H3_MAX_HEADS)
@@ -644,7 +683,11 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
     const int64_t rows = n_tokens * n_heads;
     if ((uint64_t)rows > UINT32_MAX) return fail(H3_ERR_UNSUPPORTED, "n_tokens * n_heads exceeds 2^32-1");
     const int64_t need = h3_packed_attn_backward_workspace(n_tokens, n_heads, g != nullptr);
-    if (workspace_bytes < need)
+    if (use_scratch && need > (int64_t)H3_NOALLOC_SCRATCH_BYTES)
+        return fail(H3_ERR_UNSUPPORTED, "%lld tokens x %d heads need %lld bytes of scratch; the no-allocation "
+                    "variant holds %lld (use h3_packed_attn_backward with a workspace)", (long long)n_tokens,
+                    n_heads, (long long)need, (long long)H3_NOALLOC_SCRATCH_BYTES);
+    if (!use_scratch && workspace_bytes < need)
         return fail(H3_ERR_ARG, "workspace of %lld bytes is too small: %lld needed", (long long)workspace_bytes,
                     (long long)need);
     const uint64_t bytes = (uint64_t)rows * head_dim * 2;
@@ -652,8 +695,8 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
                            range_of(o, bytes, "o", 0), range_of(dout, bytes, "dout", 0),
                            range_of(lse, (uint64_t)rows * 4, "lse", 0)};
     if (g) ins.push_back(range_of(g, bytes, "g", 0));
-    std::vector<Range> outs{range_of(dq, bytes, "dq", 0), range_of(dk, bytes, "dk", 0), range_of(dv, bytes, "dv", 0),
-                            range_of(workspace, (uint64_t)need, "workspace", 0)};
+    std::vector<Range> outs{range_of(dq, bytes, "dq", 0), range_of(dk, bytes, "dk", 0), range_of(dv, bytes, "dv", 0)};
+    if (!use_scratch) outs.push_back(range_of(workspace, (uint64_t)need, "workspace", 0));
     if (dg) outs.push_back(range_of(dg, bytes, "dg", 0));
     if ((st = check_alias(ins, outs)) != H3_OK) return st;
 
@@ -665,8 +708,6 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
     std::memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.g = g; a.o = o; a.dout = dout; a.lse = lse;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
-    a.delta = static_cast<float *>(workspace);
-    a.e = g ? static_cast<void *>(static_cast<char *>(workspace) + bwd_delta_bytes(rows)) : const_cast<void *>(dout);
     a.n_heads = (uint32_t)n_heads;
     a.n_rows = (uint32_t)rows;
     a.scale = scale;
@@ -690,6 +731,12 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
     akv.wg_prefix[n_segments] = (int32_t)total_kv;
     if (total_q > INT32_MAX || total_kv > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "too many work tiles");
 
+    // the scratch: fp32 row terms D first, then (gated) e = dout * sig(g) at a 256-byte boundary
+    if (use_scratch && (st = scratch_of_current_device(&workspace)) != H3_OK) return st;
+    a.delta = akv.delta = static_cast<float *>(workspace);
+    a.e = akv.e = g ? static_cast<void *>(static_cast<char *>(workspace) + bwd_delta_bytes(rows))
+                    : const_cast<void *>(dout);
+
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int gx_pre = 0;
@@ -711,6 +758,28 @@ h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, c
         info->bytes_written = (int64_t)(bytes * (g ? 4 : 3));
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+h3_status h3_packed_attn_backward(const void *q, const void *k, const void *v, const void *g, const void *o,
+                                  const void *dout, const float *lse, void *dq, void *dk, void *dv, void *dg,
+                                  void *workspace, int64_t workspace_bytes, int64_t n_tokens, int32_t n_heads,
+                                  int32_t head_dim, const int64_t *cu, int32_t n_segments, float scale, void *stream,
+                                  h3_plan_info *info) {
+    return attn_backward_impl(q, k, v, g, o, dout, lse, dq, dk, dv, dg, workspace, workspace_bytes, false, n_tokens,
+                              n_heads, head_dim, cu, n_segments, scale, stream, info);
+}
+
+h3_status h3_packed_attn_backward_noalloc(const void *q, const void *k, const void *v, const void *g, const void *o,
+                                          const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                          void *dg, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                          const int64_t *cu, int32_t n_segments, float scale, void *stream,
+                                          h3_plan_info *info) {
+    return attn_backward_impl(q, k, v, g, o, dout, lse, dq, dk, dv, dg, nullptr, 0, true, n_tokens, n_heads,
+                              head_dim, cu, n_segments, scale, stream, info);
 }
 
 // Shared checks of the ragged collectives: token split, channels, index range.

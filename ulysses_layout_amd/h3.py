@@ -22,12 +22,14 @@ H3_ADALN_MODULATE = 0
 H3_ADALN_GATE_RESIDUAL = 1
 H3_ADALN_GATE_MODULATE = 2
 HEAD_DIM = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20      # H3_NOALLOC_SCRATCH_BYTES
 STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3_ERR_SEGMENTS",
                 4: "H3_ERR_UNSUPPORTED", 5: "H3_ERR_ALIAS", 6: "H3_ERR_HIP"}
 
 # names every build of libh3.so must export (the declarations of include/h3.h)
 EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
            "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_packed_attn_backward_workspace",
+           "h3_packed_attn_backward_noalloc",
            "h3_adaln_segment", "h3_adaln_gate_modulate", "h3_reduce_scatter", "h3_gather_rows", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
            "h3_version")
 
@@ -87,6 +89,7 @@ def _load() -> ctypes.CDLL:
     lib.h3_packed_attn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_packed_attn_lse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_packed_attn_backward.argtypes = [vp] * 11 + [vp, i64, i64, i32, i32, i64p, i32, f32, vp, ip]
+    lib.h3_packed_attn_backward_noalloc.argtypes = [vp] * 11 + [i64, i32, i32, i64p, i32, f32, vp, ip]
     lib.h3_packed_attn_backward_workspace.argtypes = [i64, i32, i32]
     lib.h3_packed_attn_backward_workspace.restype = i64
     lib.h3_adaln_segment.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, i64p, i32, f32, vp, ip]
@@ -97,7 +100,8 @@ def _load() -> ctypes.CDLL:
     lib.h3_clip_segments.argtypes = [i64p, i32, i64, i64, ctypes.POINTER(i32), i64p, i64p]
     lib.h3_clip_segments.restype = i32
     for name in ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward",
-                 "h3_packed_attn", "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_adaln_segment",
+                 "h3_packed_attn", "h3_packed_attn_lse", "h3_packed_attn_backward",
+                 "h3_packed_attn_backward_noalloc", "h3_adaln_segment",
                  "h3_adaln_gate_modulate", "h3_reduce_scatter", "h3_gather_rows", "h3_partition"):
         getattr(lib, name).restype = ctypes.c_int
     lib.h3_status_string.argtypes = [ctypes.c_int]
@@ -331,6 +335,28 @@ def packed_attn_backward(q, k, v, g, o, dout, lse, dq, dk, dv, dg, workspace, cu
     _check(_lib.h3_packed_attn_backward(ins[0], ins[1], ins[2], gp, op, dop, lp, outs[0], outs[1], outs[2], dgp, wp,
                                         workspace.numel(), n, h, d, cu, len(cu_seqlens) - 1, float(scale),
                                         _stream_ptr(stream), ctypes.byref(info)))
+    return _info(info)
+
+
+def packed_attn_backward_noalloc(q, k, v, g, o, dout, lse, dq, dk, dv, dg, cu_seqlens: Sequence[int],
+                                 scale: float, stream=None) -> PlanInfo:
+    """``packed_attn_backward`` without a workspace: the library's per-GPU
+    scratch array (``NOALLOC_SCRATCH_BYTES``) stands in for it, so the call
+    allocates nothing.  Calls that may overlap in time on one GPU race on
+    that array."""
+    n, h, d = q.shape
+    shp = (n, h, d)
+    ins = [_dev_bf16(t, nm, shp) for t, nm in ((q, "q"), (k, "k"), (v, "v"))]
+    gp = None if g is None else _dev_bf16(g, "g", shp)
+    op, dop = _dev_bf16(o, "o", shp), _dev_bf16(dout, "dout", shp)
+    lp = _dev_f32(lse, "lse", (n, h))
+    outs = [_dev_bf16(t, nm, shp) for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    dgp = None if dg is None else _dev_bf16(dg, "dg", shp)
+    cu = _i64_array(cu_seqlens)
+    info = _PlanInfo()
+    _check(_lib.h3_packed_attn_backward_noalloc(ins[0], ins[1], ins[2], gp, op, dop, lp, outs[0], outs[1], outs[2],
+                                                dgp, n, h, d, cu, len(cu_seqlens) - 1, float(scale),
+                                                _stream_ptr(stream), ctypes.byref(info)))
     return _info(info)
 
 
