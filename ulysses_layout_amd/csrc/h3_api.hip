@@ -563,13 +563,14 @@ static h3_status packed_attn_impl(const void *q, const void *k, const void *v, c
     a.n_entries = n_segments;
     int64_t total = 0;
     double flops = 0.0;
+    const int64_t block_m = h3::packed_attn_block_m();
     for (int e = 0; e < n_segments; ++e) {
         const int s = order[e];
         const int64_t len = cu[s + 1] - cu[s];
         a.wg_prefix[e] = (int32_t)total;
         a.seg_begin[e] = (int32_t)cu[s];
         a.seg_len[e] = (int32_t)len;
-        total += ((len + h3::kAttnBlockM - 1) / h3::kAttnBlockM) * n_heads;
+        total += ((len + block_m - 1) / block_m) * n_heads;
         flops += 4.0 * head_dim * n_heads * (double)len * (double)len;
     }
     a.wg_prefix[n_segments] = (int32_t)total;

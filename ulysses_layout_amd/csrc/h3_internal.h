@@ -116,12 +116,14 @@ struct AttnArgs {
     int32_t n_entries;
     int32_t wg_prefix[kMaxSegments + 1];
     int32_t seg_begin[kMaxSegments];
-    int32_t seg_len[kMaxSegments];     // query tiles of entry e: ceil(seg_len / kAttnBlockM)
+    int32_t seg_len[kMaxSegments];     // query tiles of entry e: ceil(seg_len / packed_attn_block_m())
 };
 
-constexpr int kAttnBlockM = 256;       // query rows per workgroup (32 per wave)
 constexpr int kAttnThreads = 512;      // 8 waves
 
+// Query rows one attention workgroup covers (the kernel's tile height); the
+// host sizes the work list with it.
+int packed_attn_block_m();
 hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s);
 
 // ---- attention backward ------------------------------------------------------
