@@ -604,3 +604,82 @@ def test_noalloc_backward_rejects_alias_and_segments():
     assert rc == SEGS
     rc, _ = _attn_bwd_noalloc(mis="dq", off=-(7 << 32) + 256)     # dq moved inside q
     assert rc == ALIAS, LIB.h3_last_error()
+
+
+# ---------------------------------------------------------------------------
+# valid calls on a machine without a GPU: validation passes, the whole launch
+# plan is built (and, in a build with H3_DEBUG_BOUNDS, every kernel-argument
+# table is re-checked), and only the launch itself fails with H3_ERR_HIP
+# ---------------------------------------------------------------------------
+
+HIP_ERR = 6
+
+
+def _apart(n, base=FAKE, step=1 << 36):
+    return [base + (i + 1) * step for i in range(n)]
+
+
+def _expect_launch_failure(rc):
+    assert rc == HIP_ERR, (rc, LIB.h3_last_error())
+    msg = LIB.h3_last_error().decode()
+    assert "launch" in msg or "hipGetDevice" in msg, msg
+
+
+@fake_addresses
+@pytest.mark.parametrize("n,world,rank,planes,cap", [
+    (512, 2, -1, 3, 0), (8192, 6, 3, 3, 0), (250000, 8, 0, 4, 896_000_000), (250000, 8, -1, 4, 896_000_000),
+    (1000, 7, -1, 4, 5 * 56 * 256), (64, 56, 55, 1, 0),
+])
+def test_relayouts_reach_launch(n, world, rank, planes, cap):
+    lay = _layout(n_tokens=n, world=world, rank=rank, n_planes=planes, max_chunk_bytes=cap)
+    dst = _apart(world * planes)
+    rc, _ = _seq2head(lay, src=FAKE, dst=dst)
+    _expect_launch_failure(rc)
+    rc, _ = _seq2head_bwd(lay, grad_src=FAKE, grad_dst=dst)
+    _expect_launch_failure(rc)
+    lay1 = _layout(n_tokens=n, world=world, rank=rank, n_planes=1, max_chunk_bytes=cap)
+    rc, _ = _h2s(lay1, dst=FAKE, src=_apart(world))
+    _expect_launch_failure(rc)
+    rc, _ = _head2seq_bwd(lay1, grad_dst=FAKE, grad_src=_apart(world))
+    _expect_launch_failure(rc)
+
+
+@fake_addresses
+@pytest.mark.parametrize("cu", [(0, 96, 256, 512), (0, 98304, 131072), tuple(range(0, 257 * 3, 3)), (0, 1)])
+def test_attention_reaches_launch(cu):
+    n = cu[-1]
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    ptr = _apart(13)
+    info = _PlanInfo()
+    rc = LIB.h3_packed_attn(ptr[0], ptr[1], ptr[2], ptr[3], ptr[4], n, 14, 128, cua, len(cu) - 1, 0.088, None,
+                            ctypes.byref(info))
+    _expect_launch_failure(rc)
+    rc = LIB.h3_packed_attn_lse(ptr[0], ptr[1], ptr[2], None, ptr[4], ptr[5], n, 14, 128, cua, len(cu) - 1, 0.088,
+                                None, ctypes.byref(info))
+    _expect_launch_failure(rc)
+    ws = LIB.h3_packed_attn_backward_workspace(n, 14, 1)
+    rc = LIB.h3_packed_attn_backward(*ptr[:11], ptr[11], ws, n, 14, 128, cua, len(cu) - 1, 0.088, None,
+                                     ctypes.byref(info))
+    _expect_launch_failure(rc)
+    if ws <= h3.NOALLOC_SCRATCH_BYTES:
+        rc = LIB.h3_packed_attn_backward_noalloc(*ptr[:11], n, 14, 128, cua, len(cu) - 1, 0.088, None,
+                                                 ctypes.byref(info))
+        _expect_launch_failure(rc)
+
+
+@fake_addresses
+@pytest.mark.parametrize("a,e,c", [(0, 256, 7168), (256, 512, 7168), (100, 400, 1000), (0, 512, 8)])
+def test_token_sharded_ops_reach_launch(a, e, c):
+    cu = (0, 96, 256, 512)
+    for mode in (0, 1):
+        rc, _ = _adaln(mode=mode, x=FAKE, b=FAKE + (4 << 32) if mode else None,
+                       shift=None if mode else FAKE + (1 << 32), scale=None if mode else FAKE + (2 << 32),
+                       gate=FAKE + (5 << 32) if mode else None, y=FAKE + (3 << 32), a=a, e=e, c=c, cu=cu)
+        _expect_launch_failure(rc)
+    rc, _ = _chain(a=a, e=e, c=c, cu=cu)
+    _expect_launch_failure(rc)
+    for rank in (-1, 1):
+        rc, _ = _rs(n=e, c=c, world=3, rank=rank, partials=_apart(3), out=_apart(3, base=FAKE << 4))
+        _expect_launch_failure(rc)
+    rc, _ = _gather(n=e, c=c, world=3, shards=_apart(3), dst=FAKE)
+    _expect_launch_failure(rc)

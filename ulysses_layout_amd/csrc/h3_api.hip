@@ -27,6 +27,92 @@ h3_status ok() {
     return H3_OK;
 }
 
+// Kernel argument blocks travel by value; the kernarg segment holds 4 KB.
+static_assert(sizeof(h3::RunCopyArgs) <= 4096, "relayout arguments exceed the kernarg segment");
+static_assert(sizeof(h3::AttnArgs) <= 4096, "attention arguments exceed the kernarg segment");
+static_assert(sizeof(h3::AttnBwdArgs) <= 4096, "attention backward arguments exceed the kernarg segment");
+static_assert(sizeof(h3::AdalnArgs) <= 4096, "AdaLN arguments exceed the kernarg segment");
+static_assert(sizeof(h3::RaggedArgs) <= 4096, "ragged collective arguments exceed the kernarg segment");
+
+// ---------------------------------------------------------------------------
+// Debug builds (-DH3_DEBUG_BOUNDS) re-check every table a kernel indexes --
+// rank slots, run lengths and offsets, the attention work lists, the clipped
+// AdaLN table, the ragged row ranges -- right before its launch, against the
+// sizes the call validated, and abort with a message on the first violation.
+// Release builds compile the checks out.
+// ---------------------------------------------------------------------------
+#ifdef H3_DEBUG_BOUNDS
+[[noreturn]] void debug_bounds_fail(int line, const char *cond, const char *what) {
+    std::fprintf(stderr, "h3 debug bounds check failed (h3_api.hip:%d, %s): %s\n", line, what, cond);
+    std::fflush(stderr);
+    std::abort();
+}
+#define H3_DEBUG_CHECK(cond, what) \
+    do {                            \
+        if (!(cond)) debug_bounds_fail(__LINE__, #cond, what); \
+    } while (0)
+#define H3_DEBUG_ONLY(...) __VA_ARGS__
+
+// Relayout launch: slots 0..nr-1 each copy runs of run_vec vectors that lie
+// inside one plane row of plane_vec vectors, with a 32-bit flat index range.
+void debug_check_copy(const h3::RunCopyArgs &a, int nr, uint32_t max_run, uint32_t plane_vec) {
+    H3_DEBUG_CHECK(nr >= 1 && nr <= h3::kMaxRanks, "relayout rank slots");
+    H3_DEBUG_CHECK(a.stride_vec >= plane_vec, "relayout packed stride");
+    H3_DEBUG_CHECK(a.n_tokens >= 1, "relayout launch tokens");
+    for (int y = 0; y < nr; ++y) {
+        H3_DEBUG_CHECK(a.run_vec[y] >= 2 && a.run_vec[y] <= max_run, "relayout run length");
+        H3_DEBUG_CHECK(a.div[y].d == a.run_vec[y], "relayout divisor");
+        H3_DEBUG_CHECK((uint64_t)a.off_vec[y] + a.run_vec[y] <= plane_vec, "relayout run inside the plane row");
+        H3_DEBUG_CHECK((uint64_t)a.n_tokens * a.run_vec[y] < (1ull << 31), "relayout flat index range");
+        H3_DEBUG_CHECK(a.src_rank[y] != nullptr || a.dst_rank[y] != nullptr, "relayout rank buffer");
+    }
+    for (int y = nr; y < h3::kMaxRanks; ++y) H3_DEBUG_CHECK(a.run_vec[y] == 0, "relayout unused slot");
+}
+
+// Attention work lists: n entries, each a non-empty segment inside the
+// tokens, workgroup prefix = sum of ceil(len / block) * heads, ending at total.
+void debug_check_worklist(const int32_t *prefix, const int32_t *begin, const int32_t *len, int n, int64_t n_tokens,
+                          int64_t heads, int64_t block, int64_t total, const char *what) {
+    H3_DEBUG_CHECK(n >= 1 && n <= h3::kMaxSegments, what);
+    H3_DEBUG_CHECK(prefix[0] == 0, what);
+    int64_t covered = 0;
+    for (int e = 0; e < n; ++e) {
+        H3_DEBUG_CHECK(len[e] >= 1 && begin[e] >= 0 && (int64_t)begin[e] + len[e] <= n_tokens, what);
+        H3_DEBUG_CHECK((int64_t)prefix[e + 1] - prefix[e] == (len[e] + block - 1) / block * heads, what);
+        if (e > 0) H3_DEBUG_CHECK(len[e] <= len[e - 1], what);            // longest first
+        covered += len[e];
+    }
+    H3_DEBUG_CHECK(covered == n_tokens, what);
+    H3_DEBUG_CHECK(prefix[n] == total, what);
+}
+
+// Clipped AdaLN table: entries start at local row 0, strictly increase, end at
+// n_rows, and name increasing global segments below n_segments.
+void debug_check_adaln(const h3::AdalnArgs &a, int n_segments) {
+    H3_DEBUG_CHECK(a.n_entries >= 1 && a.n_entries <= h3::kMaxSegments, "adaln entries");
+    H3_DEBUG_CHECK(a.entry_begin[0] == 0, "adaln first entry");
+    for (int e = 0; e < a.n_entries; ++e) {
+        H3_DEBUG_CHECK(a.entry_begin[e] < a.entry_begin[e + 1], "adaln entry order");
+        H3_DEBUG_CHECK(a.entry_seg[e] >= 0 && a.entry_seg[e] < n_segments, "adaln segment id");
+        if (e > 0) H3_DEBUG_CHECK(a.entry_seg[e] > a.entry_seg[e - 1], "adaln segment order");
+    }
+    H3_DEBUG_CHECK((uint32_t)a.entry_begin[a.n_entries] == a.n_rows, "adaln last entry");
+}
+
+// Ragged collectives: every slot's row range lies inside the N x C buffer.
+void debug_check_ragged(const h3::RaggedArgs &a, int n_slots, int64_t n_tokens) {
+    H3_DEBUG_CHECK(n_slots >= 1 && n_slots <= h3::kMaxRanks, "ragged slots");
+    const uint64_t all = (uint64_t)n_tokens * a.nv_row;
+    for (int y = 0; y < n_slots; ++y) {
+        H3_DEBUG_CHECK(a.n_vec[y] >= 1 && a.n_vec[y] < (1u << 31), "ragged slot length");
+        H3_DEBUG_CHECK(a.row_vec0[y] % a.nv_row == 0 && a.n_vec[y] % a.nv_row == 0, "ragged whole rows");
+        H3_DEBUG_CHECK(a.row_vec0[y] + a.n_vec[y] <= all, "ragged slot inside the rows");
+    }
+}
+#else
+#define H3_DEBUG_ONLY(...)
+#endif
+
 // Balanced quotient/remainder split ("Distributed H3 Execution", Partition
 // Contract): the first total%parts parts hold one extra item.
 void split(int64_t total, int32_t parts, int32_t index, int64_t *begin, int64_t *count) {
@@ -270,6 +356,7 @@ h3_status h3_seq2head(const h3_layout *L, const void *src, void *const *dst, voi
                 a.dst_rank[y] = static_cast<char *>(dst[j * K + p]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
             }
             a.n_tokens = (uint32_t)nt;
+            H3_DEBUG_ONLY(debug_check_copy(a, nr, max_run, (uint32_t)L->n_heads * vec_per_head));
             int gx = 0;
             hipError_t e = h3::launch_seq2head(a, nr, max_run, s, &gx);
             if (e != hipSuccess)
@@ -344,6 +431,7 @@ h3_status h3_head2seq(const h3_layout *L, const void *const *src, void *dst, voi
             a.src_rank[y] = static_cast<const char *>(src[j]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
         }
         a.n_tokens = (uint32_t)nt;
+        H3_DEBUG_ONLY(debug_check_copy(a, nr, max_run, (uint32_t)L->n_heads * vec_per_head));
         int gx = 0;
         hipError_t e = h3::launch_head2seq(a, nr, max_run, s, &gx);
         if (e != hipSuccess) return fail(H3_ERR_HIP, "head2seq launch (chunk %d) failed: %s", c, hipGetErrorString(e));
@@ -423,6 +511,7 @@ h3_status h3_seq2head_backward(const h3_layout *L, const void *const *grad_dst, 
                 a.src_rank[y] = static_cast<const char *>(grad_dst[j * K + p]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
             }
             a.n_tokens = (uint32_t)nt;
+            H3_DEBUG_ONLY(debug_check_copy(a, nr, max_run, (uint32_t)L->n_heads * vec_per_head));
             int gx = 0;
             hipError_t e = h3::launch_head2seq(a, nr, max_run, s, &gx);
             if (e != hipSuccess)
@@ -501,6 +590,7 @@ h3_status h3_head2seq_backward(const h3_layout *L, const void *grad_dst, void *c
             a.dst_rank[y] = static_cast<char *>(grad_src[j]) + (uint64_t)t0 * hn[j] * L->head_dim * 2;
         }
         a.n_tokens = (uint32_t)nt;
+        H3_DEBUG_ONLY(debug_check_copy(a, nr, max_run, (uint32_t)L->n_heads * vec_per_head));
         int gx = 0;
         hipError_t e = h3::launch_seq2head(a, nr, max_run, s, &gx);
         if (e != hipSuccess)
@@ -575,6 +665,8 @@ static h3_status packed_attn_impl(const void *q, const void *k, const void *v, c
     }
     a.wg_prefix[n_segments] = (int32_t)total;
     if (total > INT32_MAX) return fail(H3_ERR_UNSUPPORTED, "too many work tiles");
+    H3_DEBUG_ONLY(debug_check_worklist(a.wg_prefix, a.seg_begin, a.seg_len, a.n_entries, n_tokens, n_heads, block_m,
+                                       total, "attention work list"));
     (void)hipGetLastError();
     hipError_t e = h3::launch_packed_attn(a, (int)total, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(H3_ERR_HIP, "packed attention launch failed: %s", hipGetErrorString(e));
@@ -738,6 +830,13 @@ h3_status attn_backward_impl(const void *q, const void *k, const void *v, const 
     a.e = akv.e = g ? static_cast<void *>(static_cast<char *>(workspace) + bwd_delta_bytes(rows))
                     : const_cast<void *>(dout);
 
+    H3_DEBUG_ONLY(debug_check_worklist(a.wg_prefix, a.seg_begin, a.seg_len, a.n_entries, n_tokens, n_heads,
+                                       h3::kBwdQBlock, total_q, "attention backward query work list"));
+    H3_DEBUG_ONLY(debug_check_worklist(akv.wg_prefix, akv.seg_begin, akv.seg_len, akv.n_entries, n_tokens, n_heads,
+                                       h3::kBwdKBlock, total_kv, "attention backward key work list"));
+    H3_DEBUG_ONLY(H3_DEBUG_CHECK((int64_t)a.n_rows == rows && akv.n_rows == a.n_rows, "attention backward rows"));
+    H3_DEBUG_ONLY(H3_DEBUG_CHECK(a.delta != nullptr && a.e != nullptr && akv.delta == a.delta && akv.e == a.e,
+                                 "attention backward scratch"));
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int gx_pre = 0;
@@ -846,6 +945,7 @@ h3_status h3_reduce_scatter(const void *const *partials, const void *bias, void 
     a.nv_row = (uint32_t)(channels / 8);
     if (a.nv_row >= 2) a.div_row = h3::make_fastdiv(a.nv_row);
     a.world = world;
+    H3_DEBUG_ONLY(debug_check_ragged(a, n_slots, n_tokens));
     (void)hipGetLastError();
     int gx = 0;
     hipError_t e = h3::launch_reduce_scatter(a, n_slots, max_vec, static_cast<hipStream_t>(stream), &gx);
@@ -890,6 +990,7 @@ h3_status h3_gather_rows(const void *const *shards, void *dst, int64_t n_tokens,
     a.dst_all = dst;
     a.nv_row = (uint32_t)(channels / 8);
     a.world = world;
+    H3_DEBUG_ONLY(debug_check_ragged(a, world, n_tokens));
     (void)hipGetLastError();
     int gx = 0;
     hipError_t e = h3::launch_gather_rows(a, world, max_vec, static_cast<hipStream_t>(stream), &gx);
@@ -972,6 +1073,7 @@ static h3_status adaln_impl(int32_t mode, const void *x, const void *branch, con
     }
     a.entry_begin[n] = (int32_t)n_rows;
     a.n_entries = n;
+    H3_DEBUG_ONLY(debug_check_adaln(a, n_segments));
     (void)hipGetLastError();
     int gx = 0;
     hipError_t e = h3::launch_adaln(a, static_cast<hipStream_t>(stream), &gx);

@@ -15,7 +15,9 @@ from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libh3.so")
+# H3_LIBRARY may name another build of the same library (e.g. the host-checking
+# build of build_sanitized.py); by default the in-tree release build is used.
+LIB_PATH = os.environ.get("H3_LIBRARY") or os.path.join(_PKG, "libh3.so")
 
 H3_OK = 0
 H3_ADALN_MODULATE = 0
