@@ -123,7 +123,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
 
     // ---- the wave's query rows as the B operand of S^T = K Q^T -----------------
-    // qreg[qb][ks] = Q[q0 + 16 qb + l16][32 ks + 8 grp .. +7]
+    // qreg[qb][ks] = Q[q0 + 16 qb + l16][16-byte chunk 4 grp + ks]: MFMA k step ks
+    // gives lane group g the channels of chunk 4g + ks (any assignment shared by
+    // K and Q is the same dot product; this one keeps the K reads free of LDS
+    // bank conflicts, which chunk 4 ks + g is not)
     bf16x8 qreg[kQB][kD / 32];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -132,16 +135,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(qp + (uint64_t)(valid ? q : 0) * row_stride);
 #pragma unroll
         for (int ks = 0; ks < kD / 32; ++ks) {
-            u32x4 v = src[4 * ks + grp];
+            u32x4 v = src[4 * grp + ks];
             if (!valid) v = (u32x4){0u, 0u, 0u, 0u};
             qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
     // ---- per-lane LDS offsets (independent of the tile and of the key step) ---
-    int k_off[kD / 32];                  // A operand of S^T: tile row l16 (+16 per key half), chunk 4ks + grp
+    int k_off[kD / 32];                  // A operand of S^T: tile row l16 (+16 per key half), chunk 4grp + ks
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) k_off[ks] = tile_off(l16, 4 * ks + grp);
+    for (int ks = 0; ks < kD / 32; ++ks) k_off[ks] = tile_off(l16, 4 * grp + ks);
     int v_off[kCB];                      // transposing reads: row 4 grp + l16/4 (+16), channels 16cb + 4(l16%4)
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
