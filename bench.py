@@ -397,11 +397,70 @@ def step_rates(step, ms) -> dict:
     rb = step.relayout_bytes()
     attn_tflops = step.attention_flops() / (ms["attention"] * 1e-3) / 1e12
     rel_gbps = (rb["seq2head"] + rb["head2seq"]) / ((ms["seq2head"] + ms["head2seq"]) * 1e-3) / 1e9
+    s2h_gbps = rb["seq2head"] / (ms["seq2head"] * 1e-3) / 1e9
+    h2s_gbps = rb["head2seq"] / (ms["head2seq"] * 1e-3) / 1e9
     ada_gbps = step.adaln_bytes() / (ms["adaln"] * 1e-3) / 1e9
     return {"attention_TFLOPs": attn_tflops, "attention_frac_bf16": attn_tflops / PEAK_BF16_TFLOPS,
             "relayout_GBps": rel_gbps, "relayout_frac_hbm": rel_gbps / PEAK_HBM_GBPS,
+            "seq2head_GBps": s2h_gbps, "seq2head_frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
+            "head2seq_GBps": h2s_gbps, "head2seq_frac_hbm": h2s_gbps / PEAK_HBM_GBPS,
             "adaln_GBps": ada_gbps, "adaln_frac_hbm": ada_gbps / PEAK_HBM_GBPS,
             "ms": ms}
+
+
+def oracle_sample(step, workload, budget_s: float = 2.0) -> dict:
+    """The fp64 oracle on a small bounded sample of another workload, on this
+    host's cores: its own seq2head of the attended rank from the synthetic
+    packed operand, seeded attention rows for about ``budget_s`` seconds
+    (checked against the GPU's rows of the last step), 1024 AdaLN rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.default_threads()
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    j = step.attn_ranks[0]
+    src = bits(step.qkv)
+    t0 = time.perf_counter()
+    bufs = oracle.seq2head(src, step.world, ranks=[j])
+    rel_s = time.perf_counter() - t0
+    rel_bytes = 2 * sum(b.nbytes for b in bufs.values())
+    del src
+    q, k, v = bufs[(j, 0)], bufs[(j, 1)], bufs[(j, 2)]
+    g = bufs[(j, 3)] if step.gated else None
+    cu = step.cu
+    seg_len = np.diff(np.asarray(cu))
+    rng = np.random.default_rng(workload.seed + 7)
+    flops, spent, picked = 0.0, 0.0, []
+    while spent < budget_s:
+        rows = np.sort(rng.integers(0, step.n_tokens, size=8))
+        t0 = time.perf_counter()
+        ref = oracle.attention_rows(q, k, v, g, cu, step.scale, rows=rows, threads=threads)
+        spent += time.perf_counter() - t0
+        seg_of = np.searchsorted(np.asarray(cu), rows, side="right") - 1
+        flops += float(4 * 128 * q.shape[1] * seg_len[seg_of].sum())
+        picked.append((rows, ref))
+    rows = np.concatenate([r for r, _ in picked])
+    ref = np.concatenate([x for _, x in picked])
+    got = oracle.bf16_bits_to_f64(bits(step.attn_out[j][torch.from_numpy(rows).cuda()]))
+    e = got - ref
+    n_ada = min(1024, step.tokens[0][1])
+    xb = bits(step.x[:n_ada])
+    prm = [bits(t) for t in (step.shift, step.ada_scale)]
+    t0 = time.perf_counter()
+    oracle.adaln_rows(0, xb, None, prm[0], prm[1], None, 0, n_ada, cu, step.eps, threads=threads)
+    ada_s = time.perf_counter() - t0
+    full_flops = 4.0 * 128 * q.shape[1] * float((seg_len.astype(np.float64) ** 2).sum())
+    return {"cores": threads, "kind": "oracle",
+            "relayout_GBps": rel_bytes / rel_s / 1e9, "relayout_s": rel_s,
+            "attention_GFLOPs": flops / spent / 1e9, "attention_rows": int(rows.size), "attention_s": spent,
+            "attention_full_s_extrapolated": full_flops / (flops / spent),
+            "adaln_GBps": 2 * xb.nbytes / ada_s / 1e9, "adaln_rows": n_ada,
+            "attention_parity": {"max_abs": float(np.abs(e).max()),
+                                 "rel_rms": float(np.linalg.norm(e) / np.linalg.norm(ref))},
+            "sample": f"rank {j}'s relayout by the oracle; {rows.size} seeded attention rows x {q.shape[1]} heads; "
+                      f"{n_ada} AdaLN rows"}
 
 
 # Workloads whose operands are small enough to sit largely in the 256 MB
@@ -410,7 +469,7 @@ def step_rates(step, ms) -> dict:
 CACHE_RESIDENT = ("tiny512", "8k_p6")
 
 
-def measure_workloads(names, steps: int = 5, warmup: int = 5) -> dict:
+def measure_workloads(names, steps: int = 5, warmup: int = 5, with_oracle: bool = True) -> dict:
     """The same pass at the other workloads, one after another, each freed
     before the next; reported beside the main line."""
     import torch
@@ -432,6 +491,8 @@ def measure_workloads(names, steps: int = 5, warmup: int = 5) -> dict:
                   "graph_step": measure_graph(step, steps)})
         if name in CACHE_RESIDENT:
             r["note"] = "cache-resident and latency-bound: reported, not held to the roofline targets"
+        if with_oracle:
+            r["cpu_oracle"] = oracle_sample(step, w)
         out[name] = r
         del step
         torch.cuda.empty_cache()
@@ -478,7 +539,8 @@ def main():
     graph_step = measure_graph(step, args.steps)
     backward = measure_backward(w)
     next_ops = measure_next(step)
-    workloads = measure_workloads([n for n in args.other_workloads.split(",") if n and n != w.name])
+    workloads = measure_workloads([n for n in args.other_workloads.split(",") if n and n != w.name],
+                                  with_oracle=not args.no_cpu_baseline)
 
     components = {
         "seq2head": {"ms": ms["seq2head"], "GBps": s2h_gbps, "frac_hbm": s2h_gbps / PEAK_HBM_GBPS,
