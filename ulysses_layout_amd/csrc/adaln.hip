@@ -9,10 +9,10 @@
 // One wave64 owns one row of C channels.  When C is a multiple of 512 (H3:
 // 7168 = 14 x 512) every lane owns exactly C/512 16-byte vectors of the row:
 // the wave issues all its 128-bit non-temporal loads of x (and of the branch
-// for gating), reduces the mean and then the centred second moment with
-// in-wave butterflies (no second HBM pass over x), and writes the row once.
-// The segment's parameter rows (small, [S][C], L2-resident) are staged in LDS
-// per workgroup for the plain modulation and loaded per wave elsewhere.  Other multiples of 8 take a generic path that re-reads the row.
+// for gating) together with the loads of the segment's parameter rows (small,
+// [S][C], L2-resident), reduces the mean and then the centred second moment
+// with in-wave butterflies (no LDS, no second HBM pass over x), and writes the
+// row once.  Other multiples of 8 take a generic path that re-reads the row.
 // The segment of a row comes from the clipped table in the kernel arguments
 // by a wave-uniform binary search.
 #include "h3_device.h"
@@ -49,102 +49,66 @@ __device__ __forceinline__ u32x4 gate_vec(u32x4 x, u32x4 g, u32x4 b) {
     return out;
 }
 
-// Modulation with the segment's parameter rows staged in LDS once per
-// workgroup.  The four rows of a workgroup almost always share one segment:
-// the 2*C*2 bytes of shift and scale then come from L2 once per workgroup
-// instead of once per row, and a wave holds only its row of x in registers
-// (117-124 VGPRs, so four waves per SIMD instead of two), which keeps more
-// rows in flight per CU.  A workgroup whose rows span segment boundaries
-// stages each segment in turn.  Statistics in fp32: the mean, then the
-// centred second moment, each reduced with in-wave butterflies.
+// LayerNorm of the row this wave holds in xv (lane owns vectors lane + 64 i),
+// statistics in fp32, then * (1 + scale) + shift, stored to y.  The plain
+// modulation and the gated chain both run this, so they give the same bits.
 template <int kVpl>
-__global__ __launch_bounds__(kAdalnThreads, 2) void k_adaln_modulate_lds(AdalnArgs a) {
-    __shared__ __attribute__((aligned(16))) u32x4 s_sh[kVpl * 64];
-    __shared__ __attribute__((aligned(16))) u32x4 s_sc[kVpl * 64];
-    constexpr uint32_t kRowsPerWg = kAdalnThreads / 64;
-    const uint32_t first = blockIdx.x * kRowsPerWg;
-    const uint32_t last = first + kRowsPerWg - 1 < a.n_rows ? first + kRowsPerWg - 1 : a.n_rows - 1;
-    int e0 = 0, hi = a.n_entries - 1;           // entry of the workgroup's first row
-    while (e0 < hi) {
-        const int mid = (e0 + hi + 1) >> 1;
-        if ((uint32_t)a.entry_begin[mid] <= first) e0 = mid; else hi = mid - 1;
+__device__ __forceinline__ void modulate_store(const u32x4 (&xv)[kVpl], const u32x4 *shift, const u32x4 *scale,
+                                               u32x4 *y, uint32_t channels, float eps) {
+    u32x4 sh[kVpl], sc[kVpl];
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+        sc[i] = scale[i * 64];
+        sh[i] = shift[i * 64];
     }
-    const uint32_t nv = a.channels >> 3;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s += bf16_lo(xv[i][w]) + bf16_hi(xv[i][w]);
+    const float inv_c = 1.0f / (float)channels;
+    const float mean = wave_sum(s) * inv_c;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float d0 = bf16_lo(xv[i][w]) - mean, d1 = bf16_hi(xv[i][w]) - mean;
+            q += d0 * d0 + d1 * d1;
+        }
+    const float rstd = __builtin_amdgcn_rsqf(wave_sum(q) * inv_c + eps);
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float y0 = (bf16_lo(xv[i][w]) - mean) * rstd * (1.0f + bf16_lo(sc[i][w])) + bf16_lo(sh[i][w]);
+            const float y1 = (bf16_hi(xv[i][w]) - mean) * rstd * (1.0f + bf16_hi(sc[i][w])) + bf16_hi(sh[i][w]);
+            out[w] = pack_bf16x2(y0, y1);
+        }
+        __builtin_nontemporal_store(out, y + i * 64);
+    }
+}
+
+template <int kVpl>   // exactly kVpl 16-byte vectors per lane: C = 512 * kVpl
+__global__ __launch_bounds__(kAdalnThreads) void k_adaln_modulate(AdalnArgs a) {
+    uint32_t row, seg;
+    if (!row_and_segment(a, &row, &seg)) return;
     const int lane = threadIdx.x & 63;
-    const uint32_t row = __builtin_amdgcn_readfirstlane(first + (threadIdx.x >> 6));
-    const bool has_row = row < a.n_rows;
+    const uint32_t nv = a.channels >> 3;
+    const u32x4 *x = static_cast<const u32x4 *>(a.x) + (uint64_t)row * nv + lane;
     u32x4 xv[kVpl];
-    if (has_row) {
-        const u32x4 *x = static_cast<const u32x4 *>(a.x) + (uint64_t)row * nv + lane;
 #pragma unroll
-        for (int i = 0; i < kVpl; ++i) xv[i] = __builtin_nontemporal_load(x + i * 64);
-    }
-    u32x4 *y = static_cast<u32x4 *>(a.y) + (uint64_t)row * nv + lane;
-    // one pass per segment the workgroup's rows touch (almost always one)
-    for (int e = e0; e < a.n_entries && (uint32_t)a.entry_begin[e] <= last; ++e) {
-        if (e > e0) __syncthreads();              // the previous segment's rows have read s_sh / s_sc
-        const uint64_t so = (uint64_t)a.entry_seg[e] * nv;
-        const u32x4 *shift = static_cast<const u32x4 *>(a.shift) + so;
-        const u32x4 *scale = static_cast<const u32x4 *>(a.scale) + so;
-        for (uint32_t c = threadIdx.x; c < nv; c += kAdalnThreads) {
-            s_sh[c] = shift[c];
-            s_sc[c] = scale[c];
-        }
-        __syncthreads();
-        if (!has_row || row < (uint32_t)a.entry_begin[e] || row >= (uint32_t)a.entry_begin[e + 1]) continue;
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < kVpl; ++i)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) s += bf16_lo(xv[i][w]) + bf16_hi(xv[i][w]);
-        const float inv_c = 1.0f / (float)a.channels;
-        const float mean = wave_sum(s) * inv_c;
-        // the widened row is recomputed in each pass rather than kept: 112 more
-        // registers otherwise
-#pragma unroll
-        for (int i = 0; i < kVpl; ++i) asm volatile("" : "+v"(xv[i]));
-        float q = 0.f;
-#pragma unroll
-        for (int i = 0; i < kVpl; ++i)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float d0 = bf16_lo(xv[i][w]) - mean, d1 = bf16_hi(xv[i][w]) - mean;
-                q += d0 * d0 + d1 * d1;
-            }
-        const float rstd = __builtin_amdgcn_rsqf(wave_sum(q) * inv_c + a.eps);
-#pragma unroll
-        for (int i = 0; i < kVpl; ++i) asm volatile("" : "+v"(xv[i]));
-        // parameter vectors from LDS two ahead of their use
-        u32x4 scn[2], shn[2];
-        scn[0] = s_sc[lane];
-        shn[0] = s_sh[lane];
-        if (kVpl > 1) {
-            scn[1] = s_sc[lane + 64];
-            shn[1] = s_sh[lane + 64];
-        }
-#pragma unroll
-        for (int i = 0; i < kVpl; ++i) {
-            const u32x4 sc = scn[i & 1], sh = shn[i & 1];
-            if (i + 2 < kVpl) {
-                scn[i & 1] = s_sc[lane + (i + 2) * 64];
-                shn[i & 1] = s_sh[lane + (i + 2) * 64];
-            }
-            u32x4 out;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float y0 = (bf16_lo(xv[i][w]) - mean) * rstd * (1.0f + bf16_lo(sc[w])) + bf16_lo(sh[w]);
-                const float y1 = (bf16_hi(xv[i][w]) - mean) * rstd * (1.0f + bf16_hi(sc[w])) + bf16_hi(sh[w]);
-                out[w] = pack_bf16x2(y0, y1);
-            }
-            __builtin_nontemporal_store(out, y + i * 64);
-        }
-    }
+    for (int i = 0; i < kVpl; ++i) xv[i] = __builtin_nontemporal_load(x + i * 64);
+    modulate_store<kVpl>(xv, static_cast<const u32x4 *>(a.shift) + (uint64_t)seg * nv + lane,
+                         static_cast<const u32x4 *>(a.scale) + (uint64_t)seg * nv + lane,
+                         static_cast<u32x4 *>(a.y) + (uint64_t)row * nv + lane, a.channels, a.eps);
 }
 
 // The gated residual r = x + gate[s] * b (stored rounded to bf16) and the
 // modulation of r, taken in fp32 from registers, with the next sub-block's
 // shift[s] / scale[s].  The statistics and the output take the order of
-// k_adaln_modulate_lds, so a residual that is exactly x (zero gate) gives the bits
+// modulate_store, so a residual that is exactly x (zero gate) gives the bits
 // of the plain modulation.
 template <int kVpl>
 __global__ __launch_bounds__(kAdalnThreads) void k_adaln_gate_modulate(AdalnArgs a) {
@@ -303,7 +267,7 @@ __global__ __launch_bounds__(kAdalnThreads) void k_adaln_generic(AdalnArgs a) {
 template <int kVpl>
 static void launch_exact(const AdalnArgs &a, dim3 grid, hipStream_t s) {
     if (a.mode == H3_ADALN_MODULATE)
-        hipLaunchKernelGGL(k_adaln_modulate_lds<kVpl>, grid, dim3(kAdalnThreads), 0, s, a);
+        hipLaunchKernelGGL(k_adaln_modulate<kVpl>, grid, dim3(kAdalnThreads), 0, s, a);
     else if (a.mode == H3_ADALN_GATE_RESIDUAL)
         hipLaunchKernelGGL(k_adaln_gate<kVpl>, grid, dim3(kAdalnThreads), 0, s, a);
     else
