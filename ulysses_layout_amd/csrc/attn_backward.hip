@@ -13,22 +13,20 @@
 //
 // Three launches:
 //   k_attn_bwd_pre   one 16-lane group per (token, head) row: e, dg and D.
-//   k_attn_bwd_dkdv  one workgroup per (segment, head, 128-key block).
-//                    Waves 0-3 own dK and waves 4-7 own dV of the 32-key
-//                    block w%4 (one 64-register accumulator each; the two
-//                    waves of a block share a SIMD).  The block's K and V
-//                    pass once through LDS into registers (each wave keeps
-//                    the operand it multiplies by: K for the dV wave, V for
-//                    the dK wave).  64-query tiles of Q and e stream through
-//                    LDS (buffer loads to LDS; Q triple, e double buffered),
-//                    one barrier per tile.  With the keys as MFMA columns
-//                    (lane = key), in tile t the dV wave forms S = Q K^T and
-//                    P from it (lse per row from LDS), publishes P in bf16
-//                    through LDS and adds e^T P; the dK wave forms
-//                    dS = P (dP - D) of tile t-1 from the P published then
-//                    and the dP - D it carried over the barrier, adds Q^T dS,
-//                    and forms dP - D of tile t (the accumulator seeded with
-//                    -D).  The transposing LDS load supplies e^T and Q^T.
+//   k_attn_bwd_dkdv  one workgroup per (segment, head, 192-key block).
+//                    Waves w and w+4 share a SIMD and the 48 keys of slice
+//                    w: wave w+4 accumulates dV, wave w dK (96 accumulator
+//                    registers each, v_mfma_f32_16x16x32_bf16, keys as MFMA
+//                    columns).  Each keeps the operand it multiplies by in
+//                    registers: K for the dV wave, V for the dK wave.
+//                    64-query tiles of Q and e stream through LDS (direct
+//                    buffer loads, three buffers), one barrier per tile.  In
+//                    tile t the dV wave forms S = Q K^T and P from it (lse
+//                    per row from LDS), publishes P in bf16 through LDS and
+//                    adds e^T P; the dK wave, one tile behind, forms
+//                    dP - D (the accumulator seeded with -D), dS = P (dP - D)
+//                    with the published P, and adds Q^T dS.  The transposing
+//                    LDS load supplies e^T and Q^T.
 //   k_attn_bwd_dq    the forward's structure with the roles of the operands
 //                    reassigned: one workgroup per (segment, head, 256-query
 //                    tile), lane = query.  Per 64-key tile: S^T = K Q^T and
@@ -39,13 +37,13 @@
 // are masked to -inf (dq kernel), queries there get lse = +inf so their p is 0
 // (dk/dv kernel), and no output row past the end is written.
 //
-// MFMA layouts (v_mfma_f32_32x32x16_bf16) and the transposing read follow
-// packed_attn.hip.  The streamed 64-row tiles (K and V in the dq kernel, Q and
-// e in the dk/dv kernel) use a padded LDS layout instead of the forward's XOR
-// swizzle: it is as free of bank conflicts, and because each chunk of a row
-// sits at a constant distance from the row start, one lane base and immediate
-// offsets address every read of a tile whichever buffer holds it, so the
-// single tile body computes no addresses per tile.
+// MFMA layouts and the transposing read follow packed_attn.hip.  The dk/dv
+// kernel streams its Q and e tiles in the forward's 16-row swizzled layout.
+// The dq kernel (v_mfma_f32_32x32x16_bf16) streams K and V in a padded LDS
+// layout instead: it is as free of bank conflicts, and because each chunk of a
+// row sits at a constant distance from the row start, one lane base and
+// immediate offsets address every read of a tile whichever buffer holds it,
+// so its tile body computes no addresses per tile.
 #include "h3_device.h"
 
 namespace h3 {
@@ -54,10 +52,8 @@ namespace {
 
 constexpr int kBN = 64;                  // keys per tile (dq) / queries per tile (dk/dv)
 constexpr int kWaves = kBwdThreads / 64; // 8
-constexpr int kLoadsPerKBlock = kBwdKBlock / (4 * kWaves); // per 128-row key block
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(kBwdQBlock == 32 * kWaves, "one 32-query block per wave");
-static_assert(kBwdKBlock == 32 * (kWaves / 2), "a dK wave and a dV wave per 32-key block");
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
 
@@ -154,78 +150,96 @@ __global__ __launch_bounds__(256) void k_attn_bwd_pre(AttnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: one workgroup per (segment, head, 128-key block)
+// dk, dv: one workgroup per (segment, head, 192-key block)
 // ---------------------------------------------------------------------------
+// Waves w and w + 4 share a SIMD and own the same 48 keys (three 16-key
+// blocks): wave w + 4 accumulates dV^T, wave w dK^T, 96 registers each, with
+// v_mfma_f32_16x16x32_bf16.  The keys are the MFMA columns (lane l%16 = key),
+// so every Q, e, Q^T or e^T fragment a wave reads from LDS feeds the MFMAs of
+// all three key blocks.  The dV wave holds K^T of its keys and the dK wave
+// V^T, as B operands in registers.  64-query tiles of Q and e stream through
+// LDS (direct buffer loads, the forward's 16-row swizzle, three buffers), with
+// the rows' lse (log2 units) and -D.  In tile t the dV wave forms S = Q K^T and
+// P = 2^(c S - lse) per 32-query half, publishes P (bf16) through LDS and adds
+// e^T P to dV^T; the dK wave works one tile behind: dP - D = e V^T seeded
+// with -D, dS = P (dP - D) with the P published in tile t - 1, and Q^T dS into
+// dK^T.  One barrier per tile.  P^T and dS^T as B operands come straight from
+// the C layout of S and dP (k slot j of lane group g is query 4g + j or
+// 16 + 4g + j - 4 of the half), and the transposing read supplies e^T and Q^T
+// in the same query order.
+namespace {
+constexpr int kKB2 = 3;                                  // 16-key blocks per wave
+constexpr int kKeysPerWave = 16 * kKB2;                  // 48
+constexpr int kDkdvKeys = kKeysPerWave * (kWaves / 2);   // 192 keys per workgroup
+constexpr int kTileE = kBN * kD;                         // elements of one 64-row tile
+constexpr int kLdPerTile = kBN / (4 * kWaves);           // direct loads per lane per operand and tile
+constexpr int kPVecs = 6;                                // 16-byte P vectors per lane and tile (2 halves x 3)
+static_assert(kLdPerTile * 4 * kWaves == kBN, "loads cover the tile");
+}  // namespace
+
 __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kPadTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kPadTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ2[kPadTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sE0[kPadTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t sE1[kPadTileElems];
-    __shared__ __attribute__((aligned(16))) uint32_t sP0[(kBwdKBlock / 32) * 2 * 64 * 8];
-    __shared__ __attribute__((aligned(16))) uint32_t sP1[(kBwdKBlock / 32) * 2 * 64 * 8];
-    __shared__ __attribute__((aligned(16))) float sL0[kBN];
-    __shared__ __attribute__((aligned(16))) float sL1[kBN];
-    __shared__ __attribute__((aligned(16))) float sD0[kBN];
-    __shared__ __attribute__((aligned(16))) float sD1[kBN];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[3 * kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sE[3 * kTileE];
+    __shared__ __attribute__((aligned(16))) u32x4 sP[2 * (kWaves / 2) * kPVecs * 64];
+    __shared__ __attribute__((aligned(16))) float sL[3 * kBN];
+    __shared__ __attribute__((aligned(16))) float sD[3 * kBN];
 
     const int lo = find_entry(a, blockIdx.x);
     const int seg_len = a.seg_len[lo];
-    const int kblocks = (seg_len + kBwdKBlock - 1) / kBwdKBlock;
+    const int kblocks = (seg_len + kDkdvKeys - 1) / kDkdvKeys;
     const int local = blockIdx.x - a.wg_prefix[lo];
     const int head = local / kblocks;
-    const int key0 = (local - head * kblocks) * kBwdKBlock;
-    const uint64_t row_stride = (uint64_t)a.n_heads * kD;
+    const int key0 = (local - head * kblocks) * kDkdvKeys;
+    const uint32_t n_heads = a.n_heads;
+    const float scale = a.scale, scale_log2 = a.scale_log2;
+    const float *const lse_in = a.lse;
+    const float *const delta_in = a.delta;
+    const uint64_t row_stride = (uint64_t)n_heads * kD;
     const uint64_t seg_row0 = (uint64_t)a.seg_begin[lo];
     const uint64_t base = seg_row0 * row_stride + (uint64_t)head * kD;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const int kb = wave & 3;
-    const bool dv_wave = (wave >> 2) != 0;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool dv_wave = wave >= 4;                          // wave-uniform
+    const int kbase = key0 + pair * kKeysPerWave;            // this wave's first key (segment-local)
     const int row_bytes = (int)(row_stride * 2);
 
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) + base;
-    const uint16_t *kp = static_cast<const uint16_t *>(a.k) + base;
-    const uint16_t *vp = static_cast<const uint16_t *>(a.v) + base;
     const uint16_t *ep = static_cast<const uint16_t *>(a.e) + base;
 
-    const int ld_row0 = 4 * wave + (lane >> 4);
-    const int ld_chunk = (lane & 15) ^ ((((lane >> 4) & 3) << 2) | (wave & 3));
-
-    // ---- the key block is staged through buffers that are not live yet: K rows 0-63 in sQ1, 64-127 in
-    // sQ2, V rows 0-63 in sE1, 64-127 in sP0 (viewed as bf16 rows).  It is read once, so it keeps the
-    // compact XOR-swizzled layout of h3_device.h (16 KB per 64 rows) --------------------------------
-    uint16_t *const sP0h = reinterpret_cast<uint16_t *>(sP0);
+    // K^T (dV wave) or V^T (dK wave) of the wave's keys as B operands: key 16kb + l16,
+    // MFMA k step ks on the channels of chunk 4 grp + ks (the forward's conflict-free order)
+    bf16x8 fixed_op[kKB2][kD / 32];
     {
-        const uint64_t blk0 = (uint64_t)key0 * row_stride;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(kp + blk0), 0, kBwdKBlock * row_bytes, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(vp + blk0), 0, kBwdKBlock * row_bytes, kBufferWord3);
-        const int last = seg_len - 1 - key0;
+        const uint16_t *src = static_cast<const uint16_t *>(dv_wave ? a.k : a.v) + base;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerKBlock; ++i) {
-            int key = ld_row0 + 4 * kWaves * i;
-            key = key < last ? key : last;
-            const int off = key * row_bytes + ld_chunk * 16;
-            const int lds_row = 4 * (kWaves * i + wave);             // 0..127; i < 2 -> rows < 64
-            uint16_t *kdst = (i < 2 ? sQ1 : sQ2) + (lds_row & 63) * kD;
-            uint16_t *vdst = (i < 2 ? sE1 : sP0h) + (lds_row & 63) * kD;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)kdst, 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)vdst, 16, off, 0, 0, 0);
+        for (int kb = 0; kb < kKB2; ++kb) {
+            int key = kbase + 16 * kb + l16;
+            key = key < seg_len ? key : seg_len - 1;
+            const u32x4 *row = reinterpret_cast<const u32x4 *>(src + (uint64_t)key * row_stride);
+#pragma unroll
+            for (int ks = 0; ks < kD / 32; ++ks) fixed_op[kb][ks] = __builtin_bit_cast(bf16x8, row[4 * grp + ks]);
         }
     }
-    // Q and e tiles use the padded layout: direct loads i = wave + 8m (three for waves 0-3, two for 4-7)
-    constexpr int kLdPerWave = (kPadTileLoads + kWaves - 1) / kWaves;
-    const int n_qt = (seg_len + kBN - 1) / kBN;
-    int ld_off[kLdPerWave];
+
+    // per-lane LDS offsets inside a tile
+    int a_off[kD / 32];                  // A operand (16 tile rows x 32 channels): row l16 (+16 i), chunk 4grp + ks
 #pragma unroll
-    for (int m = 0; m < kLdPerWave; ++m) {
-        int row, chunk;
-        pad_slot(wave + kWaves * m, lane, row, chunk);
-        ld_off[m] = row * row_bytes + chunk * 16;
+    for (int ks = 0; ks < kD / 32; ++ks) a_off[ks] = tile16_off(l16, 4 * grp + ks);
+    int t_off[kD / 16];                  // transposing reads: row 4grp + l16/4 (+16, +32h), channels 16cb + 4(l16%4)
+#pragma unroll
+    for (int cb = 0; cb < kD / 16; ++cb) {
+        const int col = 16 * cb + 4 * (l16 & 3);
+        t_off[cb] = tile16_off(4 * grp + (l16 >> 2), col >> 3) + (col & 7);
     }
-    auto issue_tile = [&](int qt, uint16_t *dq_, uint16_t *de_) {
+
+    // direct HBM -> LDS loads of a 64-row Q and e tile: load i of wave w covers rows
+    // 4(8i + w) .. +3, lane l row +l/16, LDS slot l; the swizzle is applied on the global side
+    const int ld_row0 = 4 * wave + (lane >> 4);
+    const int ld_chunk = (lane & 15) ^ tile16_f(ld_row0);
+    const int n_qt = (seg_len + kBN - 1) / kBN;
+    auto issue_tile = [&](int qt, int buf) __attribute__((always_inline)) {
         const uint64_t tile0 = (uint64_t)qt * kBN * row_stride;
         const __amdgpu_buffer_rsrc_t rq =
             __builtin_amdgcn_make_buffer_rsrc((void *)(qp + tile0), 0, kBN * row_bytes, kBufferWord3);
@@ -233,166 +247,202 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             __builtin_amdgcn_make_buffer_rsrc((void *)(ep + tile0), 0, kBN * row_bytes, kBufferWord3);
         const int last = seg_len - 1 - qt * kBN;
 #pragma unroll
-        for (int m = 0; m < kLdPerWave; ++m) {
-            const int i = wave + kWaves * m;                  // wave-uniform
-            if (i >= kPadTileLoads) break;
-            int off = ld_off[m];
-            if ((qt + 1) * kBN > seg_len) {
-                int row, chunk;
-                pad_slot(i, lane, row, chunk);
-                row = row < last ? row : last;
-                off = row * row_bytes + chunk * 16;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dq_ + i * 512), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(de_ + i * 512), 16, off, 0, 0, 0);
+        for (int i = 0; i < kLdPerTile; ++i) {
+            int row = ld_row0 + 4 * kWaves * i;
+            row = row < last ? row : last;
+            const int off = row * row_bytes + ld_chunk * 16;
+            const int lds_row = 4 * (kWaves * i + wave);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(sQ + buf * kTileE + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(sE + buf * kTileE + lds_row * kD), 16, off, 0, 0, 0);
         }
     };
-    auto row_value = [&](int qt) -> float {
-        const int qrow = qt * kBN + lane;
-        if (wave == 0)
-            return qrow < seg_len ? a.lse[(seg_row0 + qrow) * a.n_heads + head] * kLog2e : __builtin_inff();
-        return qrow < seg_len ? -a.delta[(seg_row0 + qrow) * a.n_heads + head] : 0.0f;
+    // waves 0 and 1 bring the tile's lse (log2 units; +inf past the end) and -D (0 past the end)
+    auto row_value = [&](int qt) __attribute__((always_inline)) -> float {
+        const int q = qt * kBN + lane;
+        const uint64_t r = (seg_row0 + (uint64_t)(q < seg_len ? q : 0)) * n_heads + head;
+        if (wave == 0) return q < seg_len ? lse_in[r] * kLog2e : __builtin_inff();
+        return q < seg_len ? -delta_in[r] : 0.0f;
     };
 
-    const int pa = pad_a_base(lane), pt = pad_t_base(lane);
-    f32x16 acc[kD / 32];
+    f32x4 acc[kD / 16][kKB2];            // dV^T or dK^T: channels 16cb + 4grp + r of key 16kb + l16
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db) acc[db] = (f32x16){};
-    bf16x8 fixed_op[kD / 16];            // K fragments of the wave's keys (dV wave) or their V fragments (dK wave)
-    f32x16 dp[2];                        // dK wave: dP - D of the previous tile, carried over the barrier
-    const int p_off = (kb * 4 * 64 + lane) * 4;
+    for (int cb = 0; cb < kD / 16; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < kKB2; ++kb) acc[cb][kb] = (f32x4){};
 
-    // dV wave, tile qt: S, P (published to pw_dst), dV += e^T P
-    auto dv_step = [&](const uint16_t *tq, const uint16_t *te, const float *tl, uint32_t *pw_dst) {
-        f32x16 sc[2] = {};
+    // A fragment (16 rows x 32 channels) and transposed A fragment (16 channels x the
+    // half's 32 rows in MFMA k-slot order) of a tile
+    auto frag = [&](const uint16_t *t, int row0, int ks) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(t + row0 * kD + a_off[ks]));
+    };
+    auto tfrag = [&](const uint16_t *t, int h, int cb) __attribute__((always_inline)) {
+        const bf16x4 x0 = lds_read_tr(t + (32 * h) * kD + t_off[cb]);
+        const bf16x4 x1 = lds_read_tr(t + (32 * h + 16) * kD + t_off[cb]);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    u32x4 *const p_pair = sP + pair * (kPVecs * 64) + lane;       // + buffer * (kWaves/2)*kPVecs*64 + vec * 64
+
+    // dV wave, tile in buffer b: S, P, publish P, dV^T += e^T P
+    auto dv_tile = [&](int b, int pb) __attribute__((always_inline)) {
+        const uint16_t *tq = sQ + b * kTileE, *te = sE + b * kTileE;
+        const float *tl = sL + b * kBN;
+        u32x4 *pout = p_pair + pb * ((kWaves / 2) * kPVecs * 64);
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
+        for (int h = 0; h < 2; ++h) {
+            f32x4 sc[2][kKB2];
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh)
-                sc[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(tq + pa + 8 * kPad4Rows * qh + 16 * ks),
-                                                                 fixed_op[ks], sc[qh], 0, 0, 0);
-        }
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-            uint32_t pw[8];
+                for (int kb = 0; kb < kKB2; ++kb) sc[i][kb] = (f32x4){};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + qh * 32 + 8 * i + 4 * half);
-                float pr[4];
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qh][4 * i + e], a.scale_log2, -lv[e]));
-                pw[2 * i] = pack_bf16x2(pr[0], pr[1]);
-                pw[2 * i + 1] = pack_bf16x2(pr[2], pr[3]);
+                for (int ks = 0; ks < kD / 32; ++ks) {
+                    const bf16x8 qf = frag(tq, 32 * h + 16 * i, ks);
+#pragma unroll
+                    for (int kb = 0; kb < kKB2; ++kb)
+                        sc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, fixed_op[kb][ks], sc[i][kb], 0, 0, 0);
+                }
+            // P = 2^(c S - lse) of queries 32h + 16i + 4grp + r
+            uint32_t w[2][kKB2][2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f32x4 lv = *reinterpret_cast<const f32x4 *>(tl + 32 * h + 16 * i + 4 * grp);
+#pragma unroll
+                for (int kb = 0; kb < kKB2; ++kb)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i][kb][2 * x], scale_log2, -lv[2 * x]));
+                        const float p1 =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i][kb][2 * x + 1], scale_log2, -lv[2 * x + 1]));
+                        w[i][kb][x] = pack_bf16x2(p0, p1);
+                    }
             }
-            *reinterpret_cast<u32x4 *>(pw_dst + p_off + qh * 512) = (u32x4){pw[0], pw[1], pw[2], pw[3]};
-            *reinterpret_cast<u32x4 *>(pw_dst + p_off + qh * 512 + 256) = (u32x4){pw[4], pw[5], pw[6], pw[7]};
+            // P^T of key block kb as a B operand, published as is for the dK wave (vector 3h + kb)
+            bf16x8 pbv[kKB2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]});
+            for (int kb = 0; kb < kKB2; ++kb) {
+                const u32x4 pv = {w[0][kb][0], w[0][kb][1], w[1][kb][0], w[1][kb][1]};
+                pout[(3 * h + kb) * 64] = pv;
+                pbv[kb] = __builtin_bit_cast(bf16x8, pv);
+            }
 #pragma unroll
-                for (int db = 0; db < kD / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        pad_tr_frag(te + pt + kPad4Rows * (8 * qh + 4 * j), db), b, acc[db], 0, 0, 0);
+            for (int cb = 0; cb < kD / 16; ++cb) {
+                const bf16x8 ef = tfrag(te, h, cb);
+#pragma unroll
+                for (int kb = 0; kb < kKB2; ++kb)
+                    acc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, pbv[kb], acc[cb][kb], 0, 0, 0);
             }
         }
     };
-    // dK wave: dS of the previous tile from its P (published last tile) and the carried dP - D, dK += Q^T dS
-    auto dk_finish = [&](const uint16_t *tq_prev, const uint32_t *p_src) {
+    // dK wave, tile in buffer b (published P in pb): dP - D, dS, dK^T += Q^T dS
+    auto dk_tile = [&](int b, int pb) __attribute__((always_inline)) {
+        const uint16_t *tq = sQ + b * kTileE, *te = sE + b * kTileE;
+        const float *td = sD + b * kBN;
+        const u32x4 *pin = p_pair + pb * ((kWaves / 2) * kPVecs * 64);
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-            const u32x4 p0 = *reinterpret_cast<const u32x4 *>(p_src + p_off + qh * 512);
-            const u32x4 p1 = *reinterpret_cast<const u32x4 *>(p_src + p_off + qh * 512 + 256);
-            const uint32_t pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            uint32_t w[8];
+        for (int h = 0; h < 2; ++h) {
+            f32x4 dp[2][kKB2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w[2 * i] = pack_bf16x2(bf16_lo(pr[2 * i]) * dp[qh][4 * i], bf16_hi(pr[2 * i]) * dp[qh][4 * i + 1]);
-                w[2 * i + 1] = pack_bf16x2(bf16_lo(pr[2 * i + 1]) * dp[qh][4 * i + 2], bf16_hi(pr[2 * i + 1]) * dp[qh][4 * i + 3]);
+            for (int i = 0; i < 2; ++i) {
+                const f32x4 nd = *reinterpret_cast<const f32x4 *>(td + 32 * h + 16 * i + 4 * grp);
+#pragma unroll
+                for (int kb = 0; kb < kKB2; ++kb) dp[i][kb] = nd;
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]});
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int db = 0; db < kD / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        pad_tr_frag(tq_prev + pt + kPad4Rows * (8 * qh + 4 * j), db), b, acc[db], 0, 0, 0);
+                for (int ks = 0; ks < kD / 32; ++ks) {
+                    const bf16x8 ef = frag(te, 32 * h + 16 * i, ks);
+#pragma unroll
+                    for (int kb = 0; kb < kKB2; ++kb)
+                        dp[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, fixed_op[kb][ks], dp[i][kb], 0, 0, 0);
+                }
+            // dS = P (dP - D), in the k-slot order of the B operand (word 2i + x of P^T)
+            bf16x8 dsb[kKB2];
+#pragma unroll
+            for (int kb = 0; kb < kKB2; ++kb) {
+                const u32x4 pv = pin[(3 * h + kb) * 64];
+                uint32_t ww[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+                        ww[2 * i + x] = pack_bf16x2(bf16_lo(pv[2 * i + x]) * dp[i][kb][2 * x],
+                                                    bf16_hi(pv[2 * i + x]) * dp[i][kb][2 * x + 1]);
+                dsb[kb] = __builtin_bit_cast(bf16x8, (u32x4){ww[0], ww[1], ww[2], ww[3]});
             }
-        }
-    };
-    // dK wave, tile qt: dP - D, seeded with -D of each register's query row
-    auto dk_start = [&](const uint16_t *te, const float *td) {
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
+            for (int cb = 0; cb < kD / 16; ++cb) {
+                const bf16x8 qf = tfrag(tq, h, cb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 nd = *reinterpret_cast<const f32x4 *>(td + qh * 32 + 8 * i + 4 * half);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dp[qh][4 * i + e] = nd[e];
+                for (int kb = 0; kb < kKB2; ++kb)
+                    acc[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, dsb[kb], acc[cb][kb], 0, 0, 0);
             }
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-#pragma unroll
-            for (int qh = 0; qh < 2; ++qh)
-                dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(te + pa + 8 * kPad4Rows * qh + 16 * ks),
-                                                                 fixed_op[ks], dp[qh], 0, 0, 0);
         }
     };
 
-    // ---- prologue ----------------------------------------------------------------------------
-    issue_tile(0, sQ0, sE0);
-    if (wave < 2) (wave == 0 ? sL0 : sD0)[lane] = row_value(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();                                  // key block and tile 0 landed
-    {
-        const uint16_t *blk = dv_wave ? (kb < 2 ? sQ1 : sQ2) : (kb < 2 ? sE1 : sP0h);
-        blk += (kb & 1) * 32 * kD;
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) fixed_op[ks] = lds_b128(blk + swz(l32, 2 * ks + half));
+    // ---- prologue: tile 0 and its row terms -----------------------------------------------------
+    issue_tile(0, 0);
+    if (wave < 2) (wave == 0 ? sL : sD)[lane] = row_value(0);
+
+    // ---- one barrier per tile; the dK wave finishes tile t - 1 in tile t ---------------------------
+    // The two kinds of wave run loops of their own (one register allocation each) that meet at
+    // the same n_qt + 1 barriers.
+    auto tile_begin = [&](int t, int b_cur, float &nv) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this lane's loads of tile t landed
+        __syncthreads();                             // ... and everyone's; P of tile t - 1 is published
+        if (t + 1 < n_qt) {
+            issue_tile(t + 1, b_cur == 2 ? 0 : b_cur + 1);
+            if (wave < 2) nv = row_value(t + 1);
+        }
+    };
+    auto tile_end = [&](int t, int b_cur, float nv) __attribute__((always_inline)) {
+        if (t + 1 < n_qt && wave < 2) (wave == 0 ? sL : sD)[(b_cur == 2 ? 0 : b_cur + 1) * kBN + lane] = nv;
+    };
+    if (dv_wave) {
+        int b_cur = 0;                               // buffer of tile t (t % 3)
+        for (int t = 0; t <= n_qt; ++t) {
+            float nv = 0.f;
+            tile_begin(t, b_cur, nv);
+            if (t < n_qt) dv_tile(b_cur, t & 1);
+            tile_end(t, b_cur, nv);
+            b_cur = b_cur == 2 ? 0 : b_cur + 1;
+        }
+    } else {
+        int b_cur = 0;
+        for (int t = 0; t <= n_qt; ++t) {
+            float nv = 0.f;
+            tile_begin(t, b_cur, nv);
+            if (t > 0) dk_tile(b_cur == 0 ? 2 : b_cur - 1, (t - 1) & 1);
+            tile_end(t, b_cur, nv);
+            b_cur = b_cur == 2 ? 0 : b_cur + 1;
+        }
     }
-    __syncthreads();                                  // the staging buffers are free again
 
-    // ---- one barrier per tile; the dK wave finishes tile qt-1 in tile qt ---------------------------
-    for (int qt = 0; qt <= n_qt; ++qt) {
-        if (qt > 0) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
+    // ---- epilogue: stage the wave's 48 output rows in LDS, store whole rows -----------------------
+    __syncthreads();                                 // every wave is done with the tiles
+    uint16_t *stage = (wave < 4 ? sQ : sE) + (wave & 3) * (kKeysPerWave * kD);
+    const float mul = dv_wave ? 1.0f : scale;
+#pragma unroll
+    for (int kb = 0; kb < kKB2; ++kb) {
+        const int r = 16 * kb + l16;
+#pragma unroll
+        for (int cb = 0; cb < kD / 16; ++cb) {
+            uint16_t *slot = stage + r * kD + (((2 * cb + (grp >> 1)) ^ l16) << 3) + 4 * (grp & 1);
+            *reinterpret_cast<u32x2 *>(slot) = (u32x2){pack_bf16x2(acc[cb][kb][0] * mul, acc[cb][kb][1] * mul),
+                                                        pack_bf16x2(acc[cb][kb][2] * mul, acc[cb][kb][3] * mul)};
         }
-        const int m3 = qt % 3;
-        const bool odd = (qt & 1) != 0;
-        uint16_t *q_cur = m3 == 0 ? sQ0 : (m3 == 1 ? sQ1 : sQ2);
-        uint16_t *q_next = m3 == 0 ? sQ1 : (m3 == 1 ? sQ2 : sQ0);
-        uint16_t *q_prev = m3 == 0 ? sQ2 : (m3 == 1 ? sQ0 : sQ1);
-        uint16_t *e_cur = odd ? sE1 : sE0, *e_next = odd ? sE0 : sE1;
-        uint32_t *p_cur = odd ? sP1 : sP0, *p_prev = odd ? sP0 : sP1;
-        const float *l_cur = odd ? sL1 : sL0, *d_cur = odd ? sD1 : sD0;
-        float nv = 0.f;
-        if (qt + 1 < n_qt) {
-            issue_tile(qt + 1, q_next, e_next);
-            if (wave < 2) nv = row_value(qt + 1);
-        }
-        if (dv_wave) {
-            if (qt < n_qt) dv_step(q_cur, e_cur, l_cur, p_cur);
-        } else {
-            if (qt > 0) dk_finish(q_prev, p_prev);
-            if (qt < n_qt) dk_start(e_cur, d_cur);
-        }
-        if (qt + 1 < n_qt && wave < 2) (wave == 0 ? (odd ? sL0 : sL1) : (odd ? sD0 : sD1))[lane] = nv;
     }
-
-    const int key = key0 + kb * 32 + l32;
-    if (key >= seg_len) return;
-    uint16_t *outp = static_cast<uint16_t *>(dv_wave ? a.dv : a.dk) + base + (uint64_t)key * row_stride;
-    const float mul = dv_wave ? 1.0f : a.scale;
+    uint16_t *outp = static_cast<uint16_t *>(dv_wave ? a.dv : a.dk) + base;
+    const int io_chunk = lane & 15;
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-            const int d0 = db * 32 + 8 * (r / 4) + 4 * half;
-            const u32x2 w = {pack_bf16x2(acc[db][r] * mul, acc[db][r + 1] * mul),
-                             pack_bf16x2(acc[db][r + 2] * mul, acc[db][r + 3] * mul)};
-            *reinterpret_cast<u32x2 *>(outp + d0) = w;
-        }
+    for (int i = 0; i < kKeysPerWave / 4; ++i) {
+        const int r = (lane >> 4) + 4 * i;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kD + ((io_chunk ^ (r & 15)) << 3));
+        const int key = kbase + r;
+        if (key < seg_len) *reinterpret_cast<u32x4 *>(outp + (uint64_t)key * row_stride + io_chunk * 8) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -544,7 +594,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     };
 
     issue_tile(0, sK0, sV0);
-    // one instance of the tile body, buffers alternating by tile parity (as in the dk/dv kernel)
+    // one instance of the tile body, buffers alternating by tile parity
     for (int kt = 0; kt < n_kt; ++kt) {
         const bool odd = (kt & 1) != 0;
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -565,6 +615,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
             *reinterpret_cast<u32x2 *>(dqp + d0) = w;
         }
 }
+
+int attn_bwd_key_block() { return kDkdvKeys; }
 
 hipError_t launch_attn_bwd_pre(const AttnBwdArgs &a, hipStream_t s, int *grid_x) {
     const uint32_t gx = (uint32_t)(((uint64_t)a.n_rows + kBwdPreRowsPerWg - 1) / kBwdPreRowsPerWg);

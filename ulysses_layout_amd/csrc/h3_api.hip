@@ -809,6 +809,7 @@ h3_status attn_backward_impl(const void *q, const void *k, const void *v, const 
     h3::AttnBwdArgs akv = a;                          // same arguments, work list over key blocks
     int64_t total_q = 0, total_kv = 0;
     double pairs = 0.0;
+    const int64_t kv_block = h3::attn_bwd_key_block();
     for (int e = 0; e < n_segments; ++e) {
         const int s = order[e];
         const int64_t len = cu[s + 1] - cu[s];
@@ -817,7 +818,7 @@ h3_status attn_backward_impl(const void *q, const void *k, const void *v, const 
         a.seg_begin[e] = akv.seg_begin[e] = (int32_t)cu[s];
         a.seg_len[e] = akv.seg_len[e] = (int32_t)len;
         total_q += ((len + h3::kBwdQBlock - 1) / h3::kBwdQBlock) * n_heads;
-        total_kv += ((len + h3::kBwdKBlock - 1) / h3::kBwdKBlock) * n_heads;
+        total_kv += ((len + kv_block - 1) / kv_block) * n_heads;
         pairs += (double)n_heads * (double)len * (double)len;
     }
     a.wg_prefix[n_segments] = (int32_t)total_q;
@@ -833,7 +834,7 @@ h3_status attn_backward_impl(const void *q, const void *k, const void *v, const 
     H3_DEBUG_ONLY(debug_check_worklist(a.wg_prefix, a.seg_begin, a.seg_len, a.n_entries, n_tokens, n_heads,
                                        h3::kBwdQBlock, total_q, "attention backward query work list"));
     H3_DEBUG_ONLY(debug_check_worklist(akv.wg_prefix, akv.seg_begin, akv.seg_len, akv.n_entries, n_tokens, n_heads,
-                                       h3::kBwdKBlock, total_kv, "attention backward key work list"));
+                                       kv_block, total_kv, "attention backward key work list"));
     H3_DEBUG_ONLY(H3_DEBUG_CHECK((int64_t)a.n_rows == rows && akv.n_rows == a.n_rows, "attention backward rows"));
     H3_DEBUG_ONLY(H3_DEBUG_CHECK(a.delta != nullptr && a.e != nullptr && akv.delta == a.delta && akv.e == a.e,
                                  "attention backward scratch"));

@@ -47,6 +47,14 @@ __device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 2) | ((r >> 2) 
 // element offset of (row r, 16-byte chunk c) inside a swizzled tile
 __device__ __forceinline__ int swz(int r, int c) { return r * kD + ((c ^ swz_f(r)) << 3); }
 
+// LDS tiles of 128-channel bf16 rows read as 16x16x32 MFMA fragments: chunk c
+// of row r sits at chunk c ^ g(r), g(r) = 2*(r%8) + (r/8)%2.  The 16 rows a
+// 16-lane group reads at one logical chunk, and the 8 rows x 2 chunks a
+// 32-lane half reads through the transposing load, then hit distinct bank
+// groups; g depends on r%16 only, so row blocks of 16 are immediate offsets.
+__device__ __forceinline__ int tile16_f(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int tile16_off(int r, int c) { return r * kD + ((c ^ tile16_f(r)) << 3); }
+
 // gfx950's transposing LDS read: per 16-lane group a 4-row x 16-channel
 // block becomes one channel x 4 rows per lane
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {

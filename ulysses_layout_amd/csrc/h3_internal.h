@@ -128,7 +128,6 @@ hipError_t launch_packed_attn(const AttnArgs &a, int n_workgroups, hipStream_t s
 
 // ---- attention backward ------------------------------------------------------
 constexpr int kBwdQBlock = 256;       // queries per workgroup of the dq kernel (8 waves x 32)
-constexpr int kBwdKBlock = 128;       // keys per workgroup of the dk/dv kernel (4 key blocks x 32)
 constexpr int kBwdThreads = 512;
 constexpr int kBwdPreRowsPerWg = 16;  // (token, head) rows per workgroup of the row-term kernel
 
@@ -148,6 +147,8 @@ struct AttnBwdArgs {
     int32_t seg_len[kMaxSegments];
 };
 
+// Keys one dk/dv workgroup covers; the host sizes that kernel's work list with it.
+int attn_bwd_key_block();
 hipError_t launch_attn_bwd_pre(const AttnBwdArgs &a, hipStream_t s, int *grid_x);
 hipError_t launch_attn_bwd_dkdv(const AttnBwdArgs &a, int n_workgroups, hipStream_t s);
 hipError_t launch_attn_bwd_dq(const AttnBwdArgs &a, int n_workgroups, hipStream_t s);

@@ -69,10 +69,6 @@ constexpr float kLazyRescale = 8.0f;               // log2 of the largest tolera
 constexpr float kMaxCheck = 128.0f;                // partial row sum that triggers the exact max (2^7 < 2^8)
 static_assert(kLoadsPerTile * 4 * kWaves == kBN, "loads cover the tile");
 
-// element offset of (row r, logical 16-byte chunk c) inside a swizzled tile
-__device__ __forceinline__ int tile_f(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kD + ((c ^ tile_f(r)) << 3); }
-
 __device__ __forceinline__ float xor_max(float v, int mask) {
     return __builtin_fmaxf(v, __shfl_xor(v, mask, 64));
 }
@@ -144,20 +140,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_packed_attn(AttnArgs a) {
     // ---- per-lane LDS offsets (independent of the tile and of the key step) ---
     int k_off[kD / 32];                  // A operand of S^T: tile row l16 (+16 per key half), chunk 4grp + ks
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) k_off[ks] = tile_off(l16, 4 * grp + ks);
+    for (int ks = 0; ks < kD / 32; ++ks) k_off[ks] = tile16_off(l16, 4 * grp + ks);
     int v_off[kCB];                      // transposing reads: row 4 grp + l16/4 (+16), channels 16cb + 4(l16%4)
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
         const int r = 4 * grp + (l16 >> 2);
         const int col = 16 * cb + 4 * (l16 & 3);
-        v_off[cb] = tile_off(r, col >> 3) + (col & 7);
+        v_off[cb] = tile16_off(r, col >> 3) + (col & 7);
     }
 
     // ---- direct HBM -> LDS tile loads ------------------------------------------
     // load i of wave `wave` covers tile rows 4*(kWaves*i + wave) .. +3, lane l row +l/16;
     // f(row) does not depend on i because rows step by 4*kWaves (a multiple of 16).
     const int ld_row0 = 4 * wave + (lane >> 4);
-    const int ld_chunk = (lane & 15) ^ tile_f(ld_row0);
+    const int ld_chunk = (lane & 15) ^ tile16_f(ld_row0);
     const int n_kt = (seg_len + kBN - 1) / kBN;
     const int row_bytes = (int)(row_stride * 2);       // <= 256 heads * 256 B
     int ld_off[kLoadsPerTile];                          // byte offsets inside a full tile
