@@ -61,10 +61,17 @@ def parse_args():
     return ap.parse_args()
 
 
+# the attention kernel's source and the headers it is compiled with
+KERNEL_SOURCES = ("ulysses_layout_amd/csrc/packed_attn.hip", "ulysses_layout_amd/csrc/h3_device.h",
+                  "ulysses_layout_amd/csrc/h3_internal.h", "include/h3.h")
+
+
 def kernel_source_digest() -> str:
-    path = os.path.join(ROOT, "ulysses_layout_amd", "csrc", "packed_attn.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(flops_per_launch: float):
