@@ -178,8 +178,16 @@ static_assert(kLdPerTile * 4 * kWaves == kBN, "loads cover the tile");
 }  // namespace
 
 __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[3 * kTileE];
-    __shared__ __attribute__((aligned(16))) uint16_t sE[3 * kTileE];
+    // Six distinct tile objects (not arrays of buffers), and loops unrolled by three so each
+    // names them statically: the compiler can then prove that the direct loads into the next
+    // tile's buffers never alias the reads of the current ones, and does not make those reads
+    // wait for the loads.
+    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ2[kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sE0[kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sE1[kTileE];
+    __shared__ __attribute__((aligned(16))) uint16_t sE2[kTileE];
     __shared__ __attribute__((aligned(16))) u32x4 sP[2 * (kWaves / 2) * kPVecs * 64];
     __shared__ __attribute__((aligned(16))) float sL[3 * kBN];
     __shared__ __attribute__((aligned(16))) float sD[3 * kBN];
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     const int ld_row0 = 4 * wave + (lane >> 4);
     const int ld_chunk = (lane & 15) ^ tile16_f(ld_row0);
     const int n_qt = (seg_len + kBN - 1) / kBN;
-    auto issue_tile = [&](int qt, int buf) __attribute__((always_inline)) {
+    auto issue_tile = [&](int qt, uint16_t *dst_q, uint16_t *dst_e) __attribute__((always_inline)) {
         const uint64_t tile0 = (uint64_t)qt * kBN * row_stride;
         const __amdgpu_buffer_rsrc_t rq =
             __builtin_amdgcn_make_buffer_rsrc((void *)(qp + tile0), 0, kBN * row_bytes, kBufferWord3);
@@ -252,16 +260,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             row = row < last ? row : last;
             const int off = row * row_bytes + ld_chunk * 16;
             const int lds_row = 4 * (kWaves * i + wave);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(sQ + buf * kTileE + lds_row * kD), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(sE + buf * kTileE + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dst_q + lds_row * kD), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void *)(dst_e + lds_row * kD), 16, off, 0, 0, 0);
         }
     };
-    // waves 0 and 1 bring the tile's lse (log2 units; +inf past the end) and -D (0 past the end)
-    auto row_value = [&](int qt) __attribute__((always_inline)) -> float {
+    // waves 0 and 1 bring the tile's lse (log2 units; +inf past the end) and -D (0 past the end):
+    // the raw entry of the lane's row (clamped) is loaded unconditionally when a trip starts and
+    // turned into the row term when it ends, so that no wait for the load (which would also
+    // wait for the tile loads issued before it) falls inside the trip's products
+    auto row_load = [&](int qt) __attribute__((always_inline)) -> float {
         const int q = qt * kBN + lane;
-        const uint64_t r = (seg_row0 + (uint64_t)(q < seg_len ? q : 0)) * n_heads + head;
-        if (wave == 0) return q < seg_len ? lse_in[r] * kLog2e : __builtin_inff();
-        return q < seg_len ? -delta_in[r] : 0.0f;
+        const uint64_t r = (seg_row0 + (uint64_t)(q < seg_len ? q : seg_len - 1)) * n_heads + head;
+        return (wave == 0 ? lse_in : delta_in)[r];
+    };
+    auto row_term = [&](int qt, float raw) __attribute__((always_inline)) -> float {
+        const bool in = qt * kBN + lane < seg_len;
+        if (wave == 0) return in ? raw * kLog2e : __builtin_inff();
+        return in ? -raw : 0.0f;
     };
 
     f32x4 acc[kD / 16][kKB2];            // dV^T or dK^T: channels 16cb + 4grp + r of key 16kb + l16
@@ -282,10 +297,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     };
     u32x4 *const p_pair = sP + pair * (kPVecs * 64) + lane;       // + buffer * (kWaves/2)*kPVecs*64 + vec * 64
 
-    // dV wave, tile in buffer b: S, P, publish P, dV^T += e^T P
-    auto dv_tile = [&](int b, int pb) __attribute__((always_inline)) {
-        const uint16_t *tq = sQ + b * kTileE, *te = sE + b * kTileE;
-        const float *tl = sL + b * kBN;
+    // dV wave, tile (tq, te) with row lse tl: S, P, publish P in buffer pb, dV^T += e^T P
+    auto dv_tile = [&](const uint16_t *tq, const uint16_t *te, const float *tl, int pb) __attribute__((always_inline)) {
         u32x4 *pout = p_pair + pb * ((kWaves / 2) * kPVecs * 64);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -335,10 +348,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
             }
         }
     };
-    // dK wave, tile in buffer b (published P in pb): dP - D, dS, dK^T += Q^T dS
-    auto dk_tile = [&](int b, int pb) __attribute__((always_inline)) {
-        const uint16_t *tq = sQ + b * kTileE, *te = sE + b * kTileE;
-        const float *td = sD + b * kBN;
+    // dK wave, tile (tq, te) with row terms -D in td (published P in buffer pb): dP - D, dS,
+    // dK^T += Q^T dS
+    auto dk_tile = [&](const uint16_t *tq, const uint16_t *te, const float *td, int pb) __attribute__((always_inline)) {
         const u32x4 *pin = p_pair + pb * ((kWaves / 2) * kPVecs * 64);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -383,65 +395,79 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_attn_bwd_dkdv(AttnBwdArgs a)
     };
 
     // ---- prologue: tile 0 and its row terms -----------------------------------------------------
-    issue_tile(0, 0);
-    if (wave < 2) (wave == 0 ? sL : sD)[lane] = row_value(0);
+    issue_tile(0, sQ0, sE0);
+    if (wave < 2) (wave == 0 ? sL : sD)[lane] = row_term(0, row_load(0));
 
     // ---- one barrier per tile; the dK wave finishes tile t - 1 in tile t ---------------------------
     // The two kinds of wave run loops of their own (one register allocation each) that meet at
-    // the same n_qt + 1 barriers.
-    auto tile_begin = [&](int t, int b_cur, float &nv) __attribute__((always_inline)) {
+    // the same n_qt + 1 barriers.  Tile t sits in buffer t % 3; trip t loads tile t + 1 into the
+    // next buffer while the dV wave reads buffer t % 3 and the dK wave buffer (t - 1) % 3.
+    auto tile_begin = [&](int t, uint16_t *nq, uint16_t *ne, float &nv) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this lane's loads of tile t landed
         __syncthreads();                             // ... and everyone's; P of tile t - 1 is published
         if (t + 1 < n_qt) {
-            issue_tile(t + 1, b_cur == 2 ? 0 : b_cur + 1);
-            if (wave < 2) nv = row_value(t + 1);
+            issue_tile(t + 1, nq, ne);
+            if (wave < 2) nv = row_load(t + 1);
         }
     };
-    auto tile_end = [&](int t, int b_cur, float nv) __attribute__((always_inline)) {
-        if (t + 1 < n_qt && wave < 2) (wave == 0 ? sL : sD)[(b_cur == 2 ? 0 : b_cur + 1) * kBN + lane] = nv;
+    auto tile_end = [&](int t, int b_next, float nv) __attribute__((always_inline)) {
+        if (t + 1 < n_qt && wave < 2) (wave == 0 ? sL : sD)[b_next * kBN + lane] = row_term(t + 1, nv);
     };
     if (dv_wave) {
-        int b_cur = 0;                               // buffer of tile t (t % 3)
-        for (int t = 0; t <= n_qt; ++t) {
+        auto trip = [&](int t, const uint16_t *cq, const uint16_t *ce, uint16_t *nq, uint16_t *ne, int b)
+            __attribute__((always_inline)) {
             float nv = 0.f;
-            tile_begin(t, b_cur, nv);
-            if (t < n_qt) dv_tile(b_cur, t & 1);
-            tile_end(t, b_cur, nv);
-            b_cur = b_cur == 2 ? 0 : b_cur + 1;
+            tile_begin(t, nq, ne, nv);
+            if (t < n_qt) dv_tile(cq, ce, sL + b * kBN, t & 1);
+            tile_end(t, b == 2 ? 0 : b + 1, nv);
+        };
+        for (int t = 0;; t += 3) {
+            trip(t, sQ0, sE0, sQ1, sE1, 0);
+            if (t == n_qt) break;
+            trip(t + 1, sQ1, sE1, sQ2, sE2, 1);
+            if (t + 1 == n_qt) break;
+            trip(t + 2, sQ2, sE2, sQ0, sE0, 2);
+            if (t + 2 == n_qt) break;
         }
     } else {
-        int b_cur = 0;
-        for (int t = 0; t <= n_qt; ++t) {
+        auto trip = [&](int t, const uint16_t *pq, const uint16_t *pe, uint16_t *nq, uint16_t *ne, int b)
+            __attribute__((always_inline)) {
             float nv = 0.f;
-            tile_begin(t, b_cur, nv);
-            if (t > 0) dk_tile(b_cur == 0 ? 2 : b_cur - 1, (t - 1) & 1);
-            tile_end(t, b_cur, nv);
-            b_cur = b_cur == 2 ? 0 : b_cur + 1;
+            tile_begin(t, nq, ne, nv);
+            if (t > 0) dk_tile(pq, pe, sD + (b == 0 ? 2 : b - 1) * kBN, (t - 1) & 1);
+            tile_end(t, b == 2 ? 0 : b + 1, nv);
+        };
+        for (int t = 0;; t += 3) {
+            trip(t, sQ2, sE2, sQ1, sE1, 0);
+            if (t == n_qt) break;
+            trip(t + 1, sQ0, sE0, sQ2, sE2, 1);
+            if (t + 1 == n_qt) break;
+            trip(t + 2, sQ1, sE1, sQ0, sE0, 2);
+            if (t + 2 == n_qt) break;
         }
     }
 
-    // ---- epilogue: stage the wave's 48 output rows in LDS, store whole rows -----------------------
+    // ---- epilogue: stage the wave's output rows in LDS 16 at a time, store whole rows --------------
     __syncthreads();                                 // every wave is done with the tiles
-    uint16_t *stage = (wave < 4 ? sQ : sE) + (wave & 3) * (kKeysPerWave * kD);
+    uint16_t *stage = (wave < 4 ? sQ0 : sE0) + (wave & 3) * (16 * kD);
     const float mul = dv_wave ? 1.0f : scale;
-#pragma unroll
-    for (int kb = 0; kb < kKB2; ++kb) {
-        const int r = 16 * kb + l16;
-#pragma unroll
-        for (int cb = 0; cb < kD / 16; ++cb) {
-            uint16_t *slot = stage + r * kD + (((2 * cb + (grp >> 1)) ^ l16) << 3) + 4 * (grp & 1);
-            *reinterpret_cast<u32x2 *>(slot) = (u32x2){pack_bf16x2(acc[cb][kb][0] * mul, acc[cb][kb][1] * mul),
-                                                        pack_bf16x2(acc[cb][kb][2] * mul, acc[cb][kb][3] * mul)};
-        }
-    }
     uint16_t *outp = static_cast<uint16_t *>(dv_wave ? a.dv : a.dk) + base;
     const int io_chunk = lane & 15;
 #pragma unroll
-    for (int i = 0; i < kKeysPerWave / 4; ++i) {
-        const int r = (lane >> 4) + 4 * i;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kD + ((io_chunk ^ (r & 15)) << 3));
-        const int key = kbase + r;
-        if (key < seg_len) *reinterpret_cast<u32x4 *>(outp + (uint64_t)key * row_stride + io_chunk * 8) = v;
+    for (int kb = 0; kb < kKB2; ++kb) {
+#pragma unroll
+        for (int cb = 0; cb < kD / 16; ++cb) {
+            uint16_t *slot = stage + l16 * kD + (((2 * cb + (grp >> 1)) ^ l16) << 3) + 4 * (grp & 1);
+            *reinterpret_cast<u32x2 *>(slot) = (u32x2){pack_bf16x2(acc[cb][kb][0] * mul, acc[cb][kb][1] * mul),
+                                                        pack_bf16x2(acc[cb][kb][2] * mul, acc[cb][kb][3] * mul)};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (lane >> 4) + 4 * i;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kD + ((io_chunk ^ r) << 3));
+            const int key = kbase + 16 * kb + r;
+            if (key < seg_len) *reinterpret_cast<u32x4 *>(outp + (uint64_t)key * row_stride + io_chunk * 8) = v;
+        }
     }
 }
 
