@@ -19,6 +19,11 @@ against the pass enqueued call by call, under ``graph_step``.  ``roofline``
 describes the dominant kernel (the attention) against MI355X's dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on this host's cores.
+
+The main line does exactly ``--warmup`` untimed passes, then times ``--steps``.
+The other workloads (``workloads``) each warm up for at least 0.25 s of passes,
+so that the power-managed clock has settled under their load, and time at
+least 5 passes and about 50 ms.
 """
 from __future__ import annotations
 
@@ -476,9 +481,28 @@ def oracle_sample(step, workload, budget_s: float = 2.0) -> dict:
 CACHE_RESIDENT = ("tiny512", "8k_p6")
 
 
-def measure_workloads(names, steps: int = 5, warmup: int = 5, with_oracle: bool = True) -> dict:
+def settle(step, warmup: int, min_seconds: float) -> float:
+    """Untimed passes: at least ``warmup`` of them and at least ``min_seconds`` of
+    wall time, so that the power-managed clock has reached its level under this
+    load (successive 32k attention calls from idle ran 1.80, 1.67, 1.64, 1.63,
+    1.60, 1.58 ms, and 1.47 ms after 0.2 s of work).  Returns seconds per pass."""
+    import torch
+
+    passes = 0
+    t0 = time.perf_counter()
+    while passes < warmup or time.perf_counter() - t0 < min_seconds:
+        step.run()
+        torch.cuda.synchronize()
+        passes += 1
+    return (time.perf_counter() - t0) / passes
+
+
+def measure_workloads(names, steps: int = 5, warmup: int = 5, with_oracle: bool = True,
+                      min_warm_s: float = 0.25, min_timed_s: float = 0.05) -> dict:
     """The same pass at the other workloads, one after another, each freed
-    before the next; reported beside the main line."""
+    before the next; reported beside the main line.  Each workload warms up
+    for at least ``warmup`` passes and ``min_warm_s`` seconds, then times at
+    least ``steps`` passes and about ``min_timed_s`` seconds of them."""
     import torch
 
     from synth import WORKLOADS
@@ -487,14 +511,16 @@ def measure_workloads(names, steps: int = 5, warmup: int = 5, with_oracle: bool 
     for name in names:
         w = WORKLOADS[name]
         step = make_step(w)
-        ms, _ = run_steps(step, steps, warmup)
+        per_pass = settle(step, warmup, min_warm_s)
+        steps_w = max(steps, min(400, int(min_timed_s / max(per_pass, 1e-6)) + 1))
+        ms, _ = run_steps(step, steps_w, 0)
         r = step_rates(step, ms)
         r.update({"n_tokens": w.n_tokens, "segments": len(w.cu) - 1, "segment_lengths": w.segment_lengths,
                   "virtual_ranks": w.world, "heads_per_rank": [c for _, c in step.heads],
                   "attention_ranks": step.attn_ranks,
                   "attention_heads": sum(step.heads[j][1] for j in step.attn_ranks), "planes": w.planes,
                   "relayout": "every rank" if w.relayout_rank < 0 else f"rank {w.relayout_rank} share",
-                  "steps": steps, "gated_by_target": name not in CACHE_RESIDENT,
+                  "steps": steps_w, "warmup_s": min_warm_s, "gated_by_target": name not in CACHE_RESIDENT,
                   "graph_step": measure_graph(step, steps)})
         if name in CACHE_RESIDENT:
             r["note"] = "cache-resident and latency-bound: reported, not held to the roofline targets"
