@@ -64,6 +64,37 @@ def test_attn_backward_ragged(lengths, gated):
     assert info.flops == 10 * 128 * h * sum(L * L for L in lengths)
 
 
+def _random_tables(count, seed):
+    """Seeded segment tables: 1-6 segments of 1-800 tokens, 1-3 heads, gated or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        lengths = [int(x) for x in rng.integers(1, 801, size=int(rng.integers(1, 7)))]
+        out.append((lengths, int(rng.integers(1, 4)), bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_TABLES = _random_tables(12, 20261203)
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_TABLES)))
+def test_attn_backward_random_tables(case):
+    """Every row of every gradient against the oracle on seeded random segment
+    tables: mixed segment lengths in one launch reach every exit point of the
+    key-block kernel's loop over query tiles (unrolled by three) and every
+    partial fill of its 48-key slices and 192-key blocks."""
+    lengths, h, gated = RANDOM_TABLES[case]
+    cu = segment_offsets(lengths)
+    n = cu[-1]
+    say("attn backward random table", case, lengths, h, gated)
+    bits = [normal_bf16_bits((n, h, 128), seed=2500 + 10 * case + i) for i in range(5)]
+    grads, _, info = _run_backward(bits, cu, gated)
+    ref = oracle.attention_backward(bits[0], bits[1], bits[2], bits[3] if gated else None, bits[4], cu, SCALE)
+    for name, got in zip(("dq", "dk", "dv", "dg"), grads):
+        _check(got, ref[name], f"{name} random table {case}")
+    assert info.flops == 10 * 128 * h * sum(L * L for L in lengths)
+
+
 @pytest.mark.parametrize("gated", [False, True])
 def test_attn_backward_one_token_segment(gated):
     """A one-token segment has p = 1, so dq = dk = 0 exactly and dv = do * sig(g).
