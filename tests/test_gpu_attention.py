@@ -51,6 +51,43 @@ def test_attention_ragged_segments(lengths, gated):
     assert info.flops == 4 * 128 * h * sum(L * L for L in lengths)
 
 
+def _random_tables(count, seed):
+    """Seeded segment tables: 1-8 segments of 1-1600 tokens, 1-4 heads, gated or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        lengths = [int(x) for x in rng.integers(1, 1601, size=int(rng.integers(1, 9)))]
+        out.append((lengths, int(rng.integers(1, 5)), bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_TABLES = _random_tables(12, 20261204)
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_TABLES)))
+def test_attention_random_tables(case):
+    """Every output row against the oracle on seeded random segment tables: mixed
+    lengths in one launch give partial query tiles, partial last key tiles and
+    waves whose rows all lie past their segment's end side by side; the row
+    log-sum-exp variant must give the same output bits."""
+    lengths, h, gated = RANDOM_TABLES[case]
+    cu = segment_offsets(lengths)
+    n = cu[-1]
+    say("attention random table", case, lengths, h, gated)
+    bits = [normal_bf16_bits((n, h, 128), seed=3100 + 10 * case + i) for i in range(4)]
+    q, k, v, g = (to_device(b) for b in bits)
+    o, info = _run(q, k, v, g if gated else None, cu)
+    ref = oracle.attention_rows(bits[0], bits[1], bits[2], bits[3] if gated else None, cu, SCALE)
+    compare(to_bits(o), ref, f"attn random table {case}")
+    assert info.flops == 4 * 128 * h * sum(L * L for L in lengths)
+    o2 = torch.empty_like(q)
+    lse = torch.empty((n, h), dtype=torch.float32, device="cuda")
+    _h3().packed_attn(q, k, v, g if gated else None, o2, cu, SCALE, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.isfinite(lse).all()
+
+
 def test_attention_peaky_softmax():
     """Q scaled by 8: large logits exercise the online-softmax rescaling."""
     cu = segment_offsets([700, 333])
