@@ -31,8 +31,8 @@ STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_ARG", 2: "H3_ERR_EMPTY_PARTITION", 3: "H3
 # names every build of libh3.so must export (the declarations of include/h3.h)
 EXPORTS = ("h3_seq2head", "h3_head2seq", "h3_seq2head_backward", "h3_head2seq_backward", "h3_packed_attn",
            "h3_packed_attn_lse", "h3_packed_attn_backward", "h3_packed_attn_backward_workspace",
-           "h3_packed_attn_backward_noalloc",
-           "h3_adaln_segment", "h3_adaln_gate_modulate", "h3_reduce_scatter", "h3_gather_rows", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
+           "h3_packed_attn_backward_noalloc", "h3_adaln_segment", "h3_adaln_gate_modulate", "h3_reduce_scatter",
+           "h3_gather_rows", "h3_partition", "h3_clip_segments", "h3_status_string", "h3_last_error",
            "h3_version")
 
 
